@@ -1,0 +1,133 @@
+/*
+ * sv_verify.h -- C ABI of the batched speculative-decoding verification
+ * library for AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the verification step of speculative decoding as the
+ * spec-verify kernel card defines it (section "Method"; operand shapes from
+ * "Usage" and "Requirements and limits"), batched over B independent
+ * sequences:
+ *
+ *   greedy  - accept draft token t_i while it equals argmax of target row
+ *             p_i (lowest index on ties); at the first miss emit that argmax
+ *             and stop; if all K match, emit argmax of p_K.
+ *   sampled - accept t_i with probability min(1, p_i(t_i)/q_i(t_i)) on
+ *             row-normalised masses (rows need not be normalised: each row's
+ *             mass is summed); on the first rejection draw the next token
+ *             from norm(max(0, p_i - q_i)); if all K are accepted draw the
+ *             bonus token from p_K.  Randomness enters only through the
+ *             caller's uniforms: u_i (i < K) drives the test of t_i and u_K
+ *             the single final draw, an inverse-CDF search in ascending token
+ *             order returning the smallest x whose running mass exceeds
+ *             u_K * (total mass).
+ *
+ * Every pointer argument of the verify calls is DEVICE memory owned by the
+ * caller (row statistics included); the library allocates nothing and keeps
+ * no pointer after returning.  Calls are asynchronous on `stream` (a
+ * hipStream_t; NULL means the default stream): outputs are valid once the
+ * stream has reached the call.  The library keeps no state between calls
+ * apart from the per-device properties it caches; calls on different streams
+ * must use different workspaces.
+ *
+ * Layouts (row-major, V contiguous, f32 = IEEE binary32):
+ *   target_probs [B, K+1, V] f32    draft_probs [B, K, V] f32
+ *   draft_tokens [B, K] int32       uniforms    [B, K+1] f32 in [0, 1)
+ *   n_accepted   [B] int32 in [0,K] next_token  [B] int32 in [0, V)
+ *   stats        [B, K+1] sv_row_stats (nullable)
+ *
+ * Preconditions that are documented, not checked on the device: all
+ * probabilities finite and >= 0, every row's mass positive, uniforms in
+ * [0, 1).  If they are violated the outputs are unspecified (no memory
+ * outside the documented buffers is touched).  A draft token outside
+ * [0, V) is defined behaviour: it is a miss (greedy) or has p(t) = q(t) = 0
+ * and is rejected (sampled).
+ */
+#ifndef SV_VERIFY_H
+#define SV_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SV_OK = 0,
+    SV_ERR_INVALID_ARG = -1,  /* NULL pointer, negative size, misaligned pointer */
+    SV_ERR_WORKSPACE = -2,    /* workspace NULL, misaligned or smaller than sv_workspace_size */
+    SV_ERR_HIP = -3,          /* a HIP runtime call or kernel launch failed */
+    SV_ERR_UNSUPPORTED = -4   /* sizes beyond the supported maximum (V > SV_MAX_V, K > SV_MAX_K) */
+} sv_status;
+
+/* Largest vocabulary and draft length the kernels accept. */
+#define SV_MAX_V 524288
+#define SV_MAX_K 4096
+
+/* Per-row statistics, one per (b, i), i in [0, K], 48 bytes.
+ *   argmax, max_p : lowest index of the maximum of p_i, and that value
+ *   sum_p, sum_q  : the masses P_i = sum_x p_i(x), Q_i = sum_x q_i(x)
+ *   sum_min       : sum_x min(p_i(x), q_i(x))
+ *   sum_pos       : sum_x max(0, p_i(x) - q_i(x))
+ *   p_t, q_t      : p_i(t_i), q_i(t_i) (0 when t_i is outside [0, V))
+ * Draft fields (sum_q, sum_min, sum_pos, q_t) are 0 for i == K and in greedy
+ * mode; p_t is 0 for i == K.  Masses are accumulated in fp64. */
+typedef struct {
+    int32_t argmax;
+    float max_p;
+    double sum_p, sum_q, sum_min, sum_pos;
+    float p_t, q_t;
+} sv_row_stats;
+
+/* Bytes of device workspace a call with these sizes needs (sampled != 0 for
+ * sv_verify_sample_batched).  Returns 0 for sizes the library rejects. */
+size_t sv_workspace_size(int32_t B, int32_t K, int32_t V, int32_t sampled);
+
+/* Zero a workspace on `stream` (a fill kernel; no memset node).  A
+ * workspace must be initialised once before its first use and again after
+ * any call that returned an error or reported a device fault through
+ * sv_workspace_error.  Every successful verify call leaves it initialised.
+ * Errors: SV_ERR_WORKSPACE for NULL or non-16-byte-aligned memory,
+ * SV_ERR_HIP when the launch fails. */
+sv_status sv_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
+
+/* Greedy verification (the card's greedy bullet).  Reads target_probs and
+ * draft_tokens; writes n_accepted, next_token and, when stats != NULL, the
+ * row statistics (sum_p, argmax, max_p, p_t).  B == 0 is a no-op that returns
+ * SV_OK without inspecting any pointer.
+ * Errors (returned before anything is launched): SV_ERR_INVALID_ARG for NULL
+ * buffers, B < 0, K < 0, V < 1 or pointers not 4-byte aligned;
+ * SV_ERR_UNSUPPORTED for V > SV_MAX_V or K > SV_MAX_K; SV_ERR_WORKSPACE for a
+ * missing or too small workspace; SV_ERR_HIP if the launch fails. */
+sv_status sv_verify_greedy_batched(const float* target_probs, const int32_t* draft_tokens,
+                                   int32_t B, int32_t K, int32_t V,
+                                   int32_t* n_accepted, int32_t* next_token,
+                                   void* workspace, size_t workspace_bytes,
+                                   sv_row_stats* stats, void* stream);
+
+/* Sampled verification (the card's speculative-sampling bullet, with the
+ * "Correctness" section's unnormalised masses).  Acceptance is decided in
+ * fp64 as u_i * q_i(t_i) * P_i < p_i(t_i) * Q_i; the residual is
+ * w(x) = max(0, p_n(x) * Q_n - q_n(x) * P_n) (P_n * Q_n times the normalised
+ * residual); if its total is 0 (rounding only) the draw uses p_n.  Same
+ * errors as the greedy call. */
+sv_status sv_verify_sample_batched(const float* target_probs, const float* draft_probs,
+                                   const int32_t* draft_tokens, const float* uniforms,
+                                   int32_t B, int32_t K, int32_t V,
+                                   int32_t* n_accepted, int32_t* next_token,
+                                   void* workspace, size_t workspace_bytes,
+                                   sv_row_stats* stats, void* stream);
+
+/* Synchronously read the workspace's device-fault word into *error_out
+ * (host memory): 0 when every call since the last sv_workspace_init
+ * completed normally, non-zero if a cross-workgroup wait exceeded its bound
+ * (the outputs of that call are then unspecified).  Waits for `stream`. */
+sv_status sv_workspace_error(const void* workspace, int32_t* error_out, void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* sv_status_string(sv_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SV_VERIFY_H */

@@ -1,0 +1,264 @@
+"""Batched speculative-decoding verification on AMD Instinct MI355X.
+
+Python binding of the C-ABI library libsv_verify.so (include/sv_verify.h).
+It marshals torch tensors into device pointers, sizes and a stream, and
+calls the library; every step of verification runs in the library's HIP
+kernels.  torch provides device memory and streams only.  There is no CPU
+path: if the library is not built, importing the binding's entry points
+raises.
+
+The operation (the spec-verify kernel card, section "Method"):
+  greedy  - accept draft token t_i while it equals the lowest-index argmax of
+            target row i; emit that argmax at the first miss, or argmax of
+            row K when all K match.
+  sampled - accept t_i with probability min(1, p_i(t_i)/q_i(t_i)) on
+            row-normalised masses; at the first rejection draw from
+            norm(max(0, p_i - q_i)); after full acceptance draw the bonus
+            from p_K; uniforms are explicit inputs (u_i for the test of t_i,
+            u_K for the final draw).
+
+Names mirror the C ABI: sv_verify_greedy_batched, sv_verify_sample_batched,
+sv_workspace_size, sv_workspace_init, sv_workspace_error, sv_status_string.
+verify_greedy / verify_sample follow the card's usage, where a 2-D
+[K+1, V] target is one sequence.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+__all__ = [
+    "SVError", "ROW_STATS_DTYPE", "library_path", "load_library",
+    "sv_workspace_size", "sv_workspace_init", "sv_workspace_error", "sv_status_string",
+    "sv_verify_greedy_batched", "sv_verify_sample_batched",
+    "verify_greedy", "verify_sample", "stats_to_numpy", "workspace_for",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libsv_verify.so")
+
+SV_OK, SV_ERR_INVALID_ARG, SV_ERR_WORKSPACE, SV_ERR_HIP, SV_ERR_UNSUPPORTED = 0, -1, -2, -3, -4
+
+# layout of sv_row_stats (48 bytes)
+ROW_STATS_DTYPE = np.dtype([
+    ("argmax", np.int32), ("max_p", np.float32),
+    ("sum_p", np.float64), ("sum_q", np.float64),
+    ("sum_min", np.float64), ("sum_pos", np.float64),
+    ("p_t", np.float32), ("q_t", np.float32),
+], align=True)
+assert ROW_STATS_DTYPE.itemsize == 48
+
+
+class SVError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {sv_status_string(status)} ({status})")
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libsv_verify.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"{_LIB_PATH} is not built; run `python -m "
+            "speculative_decoding_verification_row_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    lib.sv_workspace_size.argtypes = [I32, I32, I32, I32]
+    lib.sv_workspace_size.restype = SZ
+    lib.sv_workspace_init.argtypes = [P, SZ, P]
+    lib.sv_workspace_init.restype = ctypes.c_int
+    lib.sv_verify_greedy_batched.argtypes = [P, P, I32, I32, I32, P, P, P, SZ, P, P]
+    lib.sv_verify_greedy_batched.restype = ctypes.c_int
+    lib.sv_verify_sample_batched.argtypes = [P, P, P, P, I32, I32, I32, P, P, P, SZ, P, P]
+    lib.sv_verify_sample_batched.restype = ctypes.c_int
+    lib.sv_workspace_error.argtypes = [P, ctypes.POINTER(I32), P]
+    lib.sv_workspace_error.restype = ctypes.c_int
+    lib.sv_status_string.argtypes = [ctypes.c_int]
+    lib.sv_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def sv_status_string(status: int) -> str:
+    return load_library().sv_status_string(int(status)).decode()
+
+
+def sv_workspace_size(B: int, K: int, V: int, sampled: bool) -> int:
+    return int(load_library().sv_workspace_size(int(B), int(K), int(V), int(bool(sampled))))
+
+
+def _stream_ptr(stream, device) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(int(stream.cuda_stream))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def sv_workspace_init(workspace: torch.Tensor, stream=None) -> None:
+    with torch.cuda.device(workspace.device):
+        st = load_library().sv_workspace_init(_ptr(workspace), workspace.numel() * workspace.element_size(),
+                                              _stream_ptr(stream, workspace.device))
+    if st != SV_OK:
+        raise SVError(st, "sv_workspace_init")
+
+
+def sv_workspace_error(workspace: torch.Tensor, stream=None) -> int:
+    """Synchronously read the workspace fault word (0 = no fault)."""
+    out = ctypes.c_int32(0)
+    with torch.cuda.device(workspace.device):
+        st = load_library().sv_workspace_error(_ptr(workspace), ctypes.byref(out),
+                                               _stream_ptr(stream, workspace.device))
+    if st != SV_OK:
+        raise SVError(st, "sv_workspace_error")
+    return int(out.value)
+
+
+_WS: dict = {}
+
+
+def workspace_for(B: int, K: int, V: int, sampled: bool, device, stream=None) -> torch.Tensor:
+    """An initialised workspace for (device, stream), grown on demand.  One
+    workspace per stream: calls on different streams must not share one."""
+    device = torch.device(device)
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    key = (device.index, int(s.cuda_stream))
+    need = max(sv_workspace_size(B, K, V, sampled), 256)
+    ws = _WS.get(key)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(need, dtype=torch.uint8, device=device)
+        sv_workspace_init(ws, s)
+        _WS[key] = ws
+    return ws
+
+
+def _check(t: torch.Tensor, name: str, dtype, shape, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.device != device or t.device.type != "cuda":
+        raise ValueError(f"{name} must be on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _outputs(B, device, n_accepted, next_token):
+    if n_accepted is None:
+        n_accepted = torch.empty(B, dtype=torch.int32, device=device)
+    if next_token is None:
+        next_token = torch.empty(B, dtype=torch.int32, device=device)
+    _check(n_accepted, "n_accepted", torch.int32, (B,), device)
+    _check(next_token, "next_token", torch.int32, (B,), device)
+    return n_accepted, next_token
+
+
+def _stats_buf(stats, B, K, device):
+    if stats is True:
+        stats = torch.empty((B, K + 1, 48), dtype=torch.uint8, device=device)
+    if stats is None or stats is False:
+        return None
+    _check(stats, "stats", torch.uint8, (B, K + 1, 48), device)
+    return stats
+
+
+def sv_verify_greedy_batched(target_probs: torch.Tensor, draft_tokens: torch.Tensor,
+                             n_accepted=None, next_token=None, workspace=None,
+                             stats=None, stream=None):
+    """Greedy verification of B sequences.
+
+    target_probs [B, K+1, V] float32, draft_tokens [B, K] int32 (CUDA).
+    Returns (n_accepted [B] int32, next_token [B] int32[, stats]) on the same
+    device; `stats=True` also returns a [B, K+1, 48] uint8 tensor of
+    sv_row_stats (see stats_to_numpy)."""
+    B, K1, V = target_probs.shape
+    K = K1 - 1
+    dev = target_probs.device
+    _check(target_probs, "target_probs", torch.float32, (B, K1, V), dev)
+    _check(draft_tokens, "draft_tokens", torch.int32, (B, K), dev)
+    n_accepted, next_token = _outputs(B, dev, n_accepted, next_token)
+    st = _stats_buf(stats, B, K, dev)
+    with torch.cuda.device(dev):
+        if workspace is None:
+            workspace = workspace_for(B, K, V, False, dev, stream)
+        rc = load_library().sv_verify_greedy_batched(
+            _ptr(target_probs), _ptr(draft_tokens), B, K, V, _ptr(n_accepted), _ptr(next_token),
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(st),
+            _stream_ptr(stream, dev))
+    if rc != SV_OK:
+        raise SVError(rc, "sv_verify_greedy_batched")
+    return (n_accepted, next_token, st) if st is not None else (n_accepted, next_token)
+
+
+def sv_verify_sample_batched(target_probs: torch.Tensor, draft_probs: torch.Tensor,
+                             draft_tokens: torch.Tensor, uniforms: torch.Tensor,
+                             n_accepted=None, next_token=None, workspace=None,
+                             stats=None, stream=None):
+    """Sampled verification of B sequences.
+
+    target_probs [B, K+1, V] f32, draft_probs [B, K, V] f32, draft_tokens
+    [B, K] int32, uniforms [B, K+1] f32 in [0, 1) (CUDA).  Returns
+    (n_accepted, next_token[, stats]) like sv_verify_greedy_batched."""
+    B, K1, V = target_probs.shape
+    K = K1 - 1
+    dev = target_probs.device
+    _check(target_probs, "target_probs", torch.float32, (B, K1, V), dev)
+    _check(draft_probs, "draft_probs", torch.float32, (B, K, V), dev)
+    _check(draft_tokens, "draft_tokens", torch.int32, (B, K), dev)
+    _check(uniforms, "uniforms", torch.float32, (B, K1), dev)
+    n_accepted, next_token = _outputs(B, dev, n_accepted, next_token)
+    st = _stats_buf(stats, B, K, dev)
+    with torch.cuda.device(dev):
+        if workspace is None:
+            workspace = workspace_for(B, K, V, True, dev, stream)
+        rc = load_library().sv_verify_sample_batched(
+            _ptr(target_probs), _ptr(draft_probs), _ptr(draft_tokens), _ptr(uniforms),
+            B, K, V, _ptr(n_accepted), _ptr(next_token),
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(st),
+            _stream_ptr(stream, dev))
+    if rc != SV_OK:
+        raise SVError(rc, "sv_verify_sample_batched")
+    return (n_accepted, next_token, st) if st is not None else (n_accepted, next_token)
+
+
+def stats_to_numpy(stats: torch.Tensor) -> np.ndarray:
+    """[B, K+1, 48] uint8 device tensor -> [B, K+1] ROW_STATS_DTYPE array."""
+    a = stats.detach().cpu().contiguous().numpy()
+    return a.view(ROW_STATS_DTYPE).reshape(a.shape[:-1])
+
+
+def verify_greedy(target_probs, draft_tokens, **kw):
+    """The card's `verify_greedy(target_probs [K+1, V], draft_tokens [K])`;
+    also accepts batched [B, K+1, V] / [B, K].  Returns (n_accepted,
+    next_token) as Python ints for one sequence, tensors for a batch."""
+    if target_probs.dim() == 2:
+        out = sv_verify_greedy_batched(target_probs.unsqueeze(0), draft_tokens.reshape(1, -1), **kw)
+        return int(out[0].item()), int(out[1].item())
+    return sv_verify_greedy_batched(target_probs, draft_tokens, **kw)
+
+
+def verify_sample(target_probs, draft_probs, draft_tokens, uniforms, **kw):
+    """Sampled counterpart of verify_greedy; uniforms [K+1] (or [B, K+1])."""
+    if target_probs.dim() == 2:
+        K = target_probs.shape[0] - 1
+        out = sv_verify_sample_batched(target_probs.unsqueeze(0), draft_probs.reshape(1, K, -1),
+                                       draft_tokens.reshape(1, -1), uniforms.reshape(1, -1), **kw)
+        return int(out[0].item()), int(out[1].item())
+    return sv_verify_sample_batched(target_probs, draft_probs, draft_tokens, uniforms, **kw)

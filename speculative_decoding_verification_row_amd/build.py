@@ -1,0 +1,47 @@
+"""Build libsv_verify.so (the C-ABI library) for gfx950 with hipcc, in-tree.
+
+    python -m speculative_decoding_verification_row_amd.build [-v]
+
+The command is kept here (not in a Makefile) so the build step the tests,
+benchmark and smoke check rely on is one importable function.
+"""
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+SRC = os.path.join(PKG, "csrc", "sv_verify.hip")
+LIB = os.path.join(PKG, "libsv_verify.so")
+INCLUDE = os.path.join(ROOT, "include")
+ARCH = os.environ.get("SV_OFFLOAD_ARCH", "gfx950")
+
+
+def command(out: str) -> list:
+    return ["hipcc", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+            "-Wall", "-Wno-unused-function",
+            # packed fp32 instructions are kept out of the generated code
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-I", INCLUDE, "-o", out, SRC]
+
+
+def build(verbose: bool = False) -> str:
+    tmp = LIB + ".tmp"
+    cmd = command(tmp)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    # hipcc's host pass does not know the packed-fp32 feature name; that
+    # warning is expected and harmless
+    noise = "'-packed-fp32-ops' is not a recognized feature"
+    msgs = [l for l in (r.stdout + r.stderr).splitlines() if l.strip() and noise not in l]
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+    if verbose and msgs:
+        print("\n".join(msgs))
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,127 @@
+"""The C-ABI library builds for gfx950, loads, and exports every function that
+include/sv_verify.h declares; host-side argument validation returns its
+documented status codes before anything is launched (no GPU needed)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sv_verify.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sv_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import speculative_decoding_verification_row_amd as sv
+    if not os.path.exists(sv.library_path()):
+        from speculative_decoding_verification_row_amd import build
+        build.build()
+    return sv.load_library()
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for n in ("sv_verify_greedy_batched", "sv_verify_sample_batched", "sv_workspace_size",
+              "sv_workspace_init", "sv_workspace_error", "sv_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    import speculative_decoding_verification_row_amd as sv
+    out = subprocess.run(["nm", "-D", "--defined-only", sv.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (sv_[a-z_]+)$", out, flags=re.M))
+    for n in _declared_functions():
+        assert n in exported, n
+        assert hasattr(lib, n)
+
+
+def test_library_is_built_for_gfx950(lib):
+    import speculative_decoding_verification_row_amd as sv
+    blob = open(sv.library_path(), "rb").read()
+    # the offload bundle names its code-object target
+    assert b"amdgcn-amd-amdhsa--gfx950" in blob
+
+
+def test_status_strings(lib):
+    import speculative_decoding_verification_row_amd as sv
+    assert sv.sv_status_string(0) == "SV_OK"
+    for code in (-1, -2, -3, -4):
+        assert sv.sv_status_string(code).startswith("SV_ERR_")
+    assert "unknown" in sv.sv_status_string(7)
+
+
+def test_workspace_size(lib):
+    import speculative_decoding_verification_row_amd as sv
+    small = sv.sv_workspace_size(1, 4, 32000, True)
+    big = sv.sv_workspace_size(1024, 8, 128256, True)
+    assert 0 < small < big
+    assert big < 64 << 20                       # modest: counters and partials only
+    assert sv.sv_workspace_size(-1, 4, 100, True) == 0
+    assert sv.sv_workspace_size(1, -1, 100, True) == 0
+    assert sv.sv_workspace_size(1, 4, 0, True) == 0
+    assert sv.sv_workspace_size(1, 4, 524288, True) > 0
+    assert sv.sv_workspace_size(1, 4, 524289, True) == 0   # beyond SV_MAX_V
+    assert sv.sv_workspace_size(1, 4097, 100, True) == 0   # beyond SV_MAX_K
+
+
+FAKE = ctypes.c_void_p(0x10000)          # aligned, never dereferenced: calls below return early
+
+
+def _greedy(lib, tp=FAKE, dt=FAKE, B=1, K=1, V=8, n=FAKE, nx=FAKE, ws=FAKE, wsb=1 << 20, st=None):
+    return lib.sv_verify_greedy_batched(tp, dt, B, K, V, n, nx, ws, wsb, st, None)
+
+
+def _sample(lib, tp=FAKE, dp=FAKE, dt=FAKE, u=FAKE, B=1, K=1, V=8, n=FAKE, nx=FAKE, ws=FAKE,
+            wsb=1 << 20, st=None):
+    return lib.sv_verify_sample_batched(tp, dp, dt, u, B, K, V, n, nx, ws, wsb, st, None)
+
+
+def test_argument_errors_greedy(lib):
+    assert _greedy(lib, tp=None) == -1
+    assert _greedy(lib, dt=None) == -1
+    assert _greedy(lib, n=None) == -1
+    assert _greedy(lib, nx=None) == -1
+    assert _greedy(lib, B=-1) == -1
+    assert _greedy(lib, K=-1) == -1
+    assert _greedy(lib, V=0) == -1
+    assert _greedy(lib, tp=ctypes.c_void_p(0x10002)) == -1          # not 4-byte aligned
+    assert _greedy(lib, st=ctypes.c_void_p(0x10004)) == -1          # stats not 8-byte aligned
+    assert _greedy(lib, V=524289) == -4
+    assert _greedy(lib, K=4097) == -4
+    assert _greedy(lib, ws=None) == -2
+    assert _greedy(lib, ws=ctypes.c_void_p(0x10008)) == -2          # not 16-byte aligned
+    assert _greedy(lib, wsb=16) == -2
+    # K = 0 needs no draft tokens; B = 0 is a no-op
+    assert _greedy(lib, dt=None, K=0, B=0) == 0
+    assert _greedy(lib, B=0) == 0
+
+
+def test_argument_errors_sampled(lib):
+    assert _sample(lib, tp=None) == -1
+    assert _sample(lib, dp=None) == -1
+    assert _sample(lib, dt=None) == -1
+    assert _sample(lib, u=None) == -1
+    assert _sample(lib, B=-3) == -1
+    assert _sample(lib, V=-5) == -1
+    assert _sample(lib, u=ctypes.c_void_p(0x10001)) == -1
+    assert _sample(lib, V=600000) == -4
+    assert _sample(lib, wsb=0) == -2
+    assert _sample(lib, dp=None, dt=None, K=0, B=0) == 0
+    assert _sample(lib, B=0) == 0
+
+
+def test_binding_without_library_fails_loudly(monkeypatch, tmp_path):
+    import speculative_decoding_verification_row_amd as sv
+    monkeypatch.setattr(sv, "_lib", None)
+    monkeypatch.setattr(sv, "_LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        sv.load_library()

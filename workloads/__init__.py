@@ -248,3 +248,37 @@ def formula_bytes(B: int, K: int, V: int, sampled: bool) -> int:
     plus K*V*4 when the draft rows are read (sampled mode)."""
     per = (K + 1) * V * 4 + (K * V * 4 if sampled else 0)
     return B * per
+
+
+def _gen_one(args):
+    family, b, B, K, V, seed, rnd = args
+    p, q, t, u, info = gen_sequence(family, b, B, K, V, seed, rnd)
+    return b, p, q, t, u, info
+
+
+def iter_sequences(family: str, B: int, K: int, V: int, seed: int = 0, rnd: int = 0,
+                   seqs=None, workers: int = 1):
+    """Yield (b, p, q, t, u, info) for each requested sequence, in order,
+    generating them in `workers` forked processes when workers > 1."""
+    idx = list(range(B)) if seqs is None else [int(s) for s in seqs]
+    jobs = [(family, b, B, K, V, seed, rnd) for b in idx]
+    if workers <= 1 or len(jobs) <= 1:
+        for j in jobs:
+            yield _gen_one(j)
+        return
+    import multiprocessing as mp
+    ctx = mp.get_context("fork")
+    with ctx.Pool(processes=workers) as pool:
+        for r in pool.imap(_gen_one, jobs, chunksize=1):
+            yield r
+
+
+def default_workers() -> int:
+    """Worker processes for generation: the CPUs this process may use, capped
+    at 16."""
+    import os
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
