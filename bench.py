@@ -1,0 +1,228 @@
+"""Benchmark of the batched verification step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
+                    [--mode sampled|greedy] [--no-cpu-baseline]
+
+One step = one call of the verification library over a whole batch (all
+rows of all B sequences: the fused row pass, the acceptance decisions, the
+accept-prefix scan and the final draw).  Inputs are generated on the host by
+the seeded workload generator, copied to HBM before timing, and two input
+sets alternate so that consecutive steps never hit the same data in the
+256 MB Infinity Cache.
+
+Printed: one JSON line (rank 0) with verify rounds/s as `value`, the
+roofline of the dominant kernel (formula bytes per launch over the kernel's
+average HIP-event duration on its own stream, against 8 TB/s), and the fp64
+CPU oracle timed on the host's cores on a bounded sample of the same
+workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "speculative_decoding_verification_row_amd", "csrc", "sv_verify.hip")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_sha256() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_for(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, or None if
+    none were taken or the kernel source changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = data.get(f"{kernel}|{workload}")
+    if not e or e.get("source_sha256") != source_sha256():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, mode, target_seconds=10.0):
+    """Time the fp64 oracle as it stands on this host's cores over a bounded
+    sample of the workload (whole sequences of round 0), scaled to rounds/s."""
+    import numpy as np
+    import oracle
+    import workloads
+    cores = workloads.default_workers()
+    B = cfg["B"]
+    n_seq = min(B, max(1, 2 * cores))
+    seqs = list(range(n_seq))
+    hb = workloads.make_batch(cfg["family"], B, cfg["K"], cfg["V"], seed=0, seqs=seqs)
+    sampled = mode == "sampled"
+
+    def once():
+        if sampled:
+            oracle.verify_sample(hb.target_probs, hb.draft_probs, hb.draft_tokens, hb.uniforms,
+                                 threads=cores, diagnostics=False)
+        else:
+            oracle.verify_greedy(hb.target_probs, hb.draft_tokens, threads=cores)
+
+    once()
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        once()
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= target_seconds:
+            break
+    seq_per_s = reps * n_seq / el
+    return {"value": seq_per_s / B, "unit": "rounds/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n_seq} of {B} sequences of round 0, repeated {reps}x in {el:.1f}s, "
+                      f"scaled by {n_seq}/{B} to whole rounds"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--workload", type=int, default=3)
+    ap.add_argument("--mode", default=None, choices=[None, "sampled", "greedy"])
+    ap.add_argument("--sets", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the verification step is sharded over sequences with "
+              "no exchange, and this build runs on a single MI355X; use --gpus 1.", flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import workloads
+    from workloads.device import device_batch
+    import speculative_decoding_verification_row_amd as sv
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP device", flush=True)
+        sys.exit(1)
+    sv.load_library()
+    cfg = dict(workloads.CONFIGS[args.workload])
+    mode = args.mode or ("sampled" if "sampled" in cfg["modes"] else "greedy")
+    sampled = mode == "sampled"
+    B, K, V = cfg["B"], cfg["K"], cfg["V"]
+    dev = torch.device("cuda:0")
+    workload = f"B={B} K={K} V={V} {mode}"
+    log(f"workload {args.workload}: {workload}; generating {args.sets} input sets")
+
+    sets = []
+    for s in range(args.sets):
+        sets.append(device_batch(cfg["family"], B, K, V, seed=s, device=dev, sampled=sampled))
+        log(f"  set {s} ready ({sets[-1]['sha256'][:12]})")
+    n_out = torch.empty(B, dtype=torch.int32, device=dev)
+    x_out = torch.empty(B, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    ws = sv.workspace_for(B, K, V, sampled, dev, stream)
+
+    def step(db):
+        if sampled:
+            sv.sv_verify_sample_batched(db["tp"], db["dp"], db["dt"], db["u"], n_accepted=n_out,
+                                        next_token=x_out, workspace=ws, stream=stream)
+        else:
+            sv.sv_verify_greedy_batched(db["tp"], db["dt"], n_accepted=n_out, next_token=x_out,
+                                        workspace=ws, stream=stream)
+
+    for w in range(args.warmup):
+        step(sets[w % len(sets)])
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} done; timing {args.steps} steps")
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        ev[k][0].record(stream)
+        step(sets[k % len(sets)])
+        ev[k][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = [a.elapsed_time(b) for a, b in ev]
+    avg_ms = float(np.mean(kernel_ms))
+    med_ms = float(np.median(kernel_ms))
+    assert sv.sv_workspace_error(ws) == 0, "device fault word set during the benchmark"
+
+    # spot check of the last step's outputs against the oracle (2 sequences)
+    last = sets[(args.steps - 1) % len(sets)]
+    spot = spot_check(cfg, mode, last, n_out, x_out, seed=(args.steps - 1) % len(sets))
+
+    fbytes = workloads.formula_bytes(B, K, V, sampled)
+    achieved = fbytes / (avg_ms * 1e-3) / 1e9
+    kernel = "sv_sample_kernel" if sampled else "sv_greedy_kernel"
+    rounds_per_s = args.steps / wall
+    line = {
+        "metric": "verify rounds/s + HBM GB/s (% of peak), B=256 K=5 V=128256 sampled",
+        "value": round(rounds_per_s, 2),
+        "unit": "rounds/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": workload, "B": B, "K": K, "V": V, "mode": mode,
+                   "recipe": cfg["family"], "input_sets": args.sets},
+        "hbm_gbs": round(fbytes * rounds_per_s / 1e9, 1),
+        "pct_of_peak": round(100.0 * fbytes * rounds_per_s / 1e9 / PEAK_HBM_GBS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": traffic_for(kernel, workload),
+                     "kernel": kernel, "kernel_avg_us": round(avg_ms * 1e3, 2),
+                     "kernel_median_us": round(med_ms * 1e3, 2),
+                     "algorithmic_bytes_per_launch": fbytes},
+        "accumulation": "f64",
+        "parity_spot": spot,
+        "context": {"pages_cpu_latency_us": {"greedy": 33, "sampled": 117,
+                                             "hardware": "Raspberry Pi 5, V=32000, K=4, one sequence"}},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle baseline")
+        line["cpu_baseline"] = cpu_baseline(cfg, mode)
+    print(json.dumps(line), flush=True)
+
+
+def spot_check(cfg, mode, db, n_out, x_out, seed):
+    import numpy as np
+    import oracle
+    import workloads
+    seqs = [0, cfg["B"] - 1]
+    hb = workloads.make_batch(cfg["family"], cfg["B"], cfg["K"], cfg["V"], seed=seed, seqs=seqs)
+    n = n_out.cpu().numpy()[seqs]
+    x = x_out.cpu().numpy()[seqs]
+    if mode == "sampled":
+        o = oracle.verify_sample(hb.target_probs, hb.draft_probs, hb.draft_tokens, hb.uniforms)
+        d = o["diag"]
+        bnd = (d["accept_margin"] <= 1e-5) | (d["draw_margin"] <= 1e-5)
+    else:
+        o = oracle.verify_greedy(hb.target_probs, hb.draft_tokens)
+        bnd = np.zeros(len(seqs), bool)
+    ok = (n == o["n_accepted"]) & (x == o["next_token"])
+    if not np.all(ok | bnd):
+        raise SystemExit(f"benchmark outputs differ from the oracle: gpu {n},{x} oracle "
+                         f"{o['n_accepted']},{o['next_token']}")
+    return f"{int(ok.sum())}/{len(seqs)} sequences identical to the oracle ({int(bnd.sum())} boundary)"
+
+
+if __name__ == "__main__":
+    main()

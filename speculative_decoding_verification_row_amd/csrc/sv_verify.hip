@@ -121,38 +121,69 @@ struct Args {
     unsigned long long wait_ticks;   // wait bound in wall-clock ticks
 };
 
-// ------------------------------------------------------------ atomics --
+// ------------------------------------------- cross-block communication --
+//
+// Every value one block publishes for another (chunk partials, row results,
+// prefixes, counters, flags) is written and read with agent-scope atomic
+// accesses.  On gfx950 these are performed at the device-coherent level
+// (sc1 loads and stores; RMW atomics at the memory side) instead of in the
+// per-XCD L2, so no L2 write-back or invalidate (the cost of agent-scope
+// release/acquire fences) is ever needed.  Ordering is explicit:
+//   writer: data stores -> publish() -> counter RMW or flag store
+//   reader: counter RMW or flag load -> observe() -> data loads
+// publish() waits for the wave's outstanding memory operations to complete
+// (gfx9 counts stores in vmcnt); both are compiler barriers.
 
-__device__ __forceinline__ unsigned add_acq_rel(unsigned* p, unsigned v)
+__device__ __forceinline__ void publish() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void observe() { asm volatile("" ::: "memory"); }
+
+__device__ __forceinline__ unsigned count_up(unsigned* p)
 {
-    return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    return __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-
-__device__ __forceinline__ unsigned load_relaxed(const unsigned* p)
+__device__ __forceinline__ void put_u32(void* p, unsigned v)
 {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(static_cast<unsigned*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-
-__device__ __forceinline__ void store_release(unsigned* p, unsigned v)
+__device__ __forceinline__ unsigned get_u32(const void* p)
 {
-    __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    return __hip_atomic_load(static_cast<const unsigned*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-
-__device__ __forceinline__ void fence_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+__device__ __forceinline__ void put_u64(void* p, unsigned long long v)
+{
+    __hip_atomic_store(static_cast<unsigned long long*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned long long get_u64(const void* p)
+{
+    return __hip_atomic_load(static_cast<const unsigned long long*>(p), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void put_i32(int* p, int v) { put_u32(p, (unsigned)v); }
+__device__ __forceinline__ int get_i32(const int* p) { return (int)get_u32(p); }
+__device__ __forceinline__ void put_f32(float* p, float v) { put_u32(p, __float_as_uint(v)); }
+__device__ __forceinline__ float get_f32(const float* p) { return __uint_as_float(get_u32(p)); }
+__device__ __forceinline__ void put_f64(double* p, double v)
+{
+    put_u64(p, (unsigned long long)__double_as_longlong(v));
+}
+__device__ __forceinline__ double get_f64(const double* p)
+{
+    return __longlong_as_double((long long)get_u64(p));
+}
 
 // Bounded wait for a row flag; on expiry raises the fault word and returns
 // (the call's outputs are then unspecified, but every block still exits).
 __device__ __forceinline__ void wait_flag(const unsigned* flag, Header* hdr, unsigned long long ticks)
 {
     const unsigned long long t0 = wall_clock64();
-    while (load_relaxed(flag) == 0u) {
+    while (get_u32(flag) == 0u) {
         __builtin_amdgcn_s_sleep(2);
         if (wall_clock64() - t0 > ticks) {
-            __hip_atomic_store(&hdr->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            put_u32(&hdr->error, 1u);
             break;
         }
     }
-    fence_acquire();
+    observe();
 }
 
 // Wave-cooperative zeroing of [p, p + bytes), p 8-byte aligned, bytes % 8 == 0.
@@ -160,7 +191,7 @@ __device__ __forceinline__ void wave_zero(void* p, size_t bytes)
 {
     unsigned long long* q = static_cast<unsigned long long*>(p);
     const size_t n = bytes / 8;
-    for (size_t j = threadIdx.x & 63; j < n; j += 64) q[j] = 0ull;
+    for (size_t j = threadIdx.x & 63; j < n; j += 64) put_u64(q + j, 0ull);
 }
 
 // Once sequence b is resolved nothing reads its partials, prefixes or row
@@ -351,9 +382,18 @@ __device__ __forceinline__ void combine_row(const Args& a, int b, int i, int64_t
     const int lane = threadIdx.x & 63;
     const int NC = a.NC, K = a.K, V = a.V;
     const bool pair = SAMPLED && i < K;
-    fence_acquire();
+    observe();
     ChunkPart cp{0.0, 0.0, 0.0, -INFINITY, INT_MAX};
-    if (lane < NC) cp = a.parts[row * NC + lane];
+    if (lane < NC) {
+        const ChunkPart* src = &a.parts[row * NC + lane];
+        cp.sp = get_f64(&src->sp);
+        if (pair) {
+            cp.sq = get_f64(&src->sq);
+            cp.smin = get_f64(&src->smin);
+        }
+        cp.maxv = get_f32(&src->maxv);
+        cp.arg = get_i32(&src->arg);
+    }
     float mv = cp.maxv;
     int ai = cp.arg;
 #pragma unroll
@@ -371,33 +411,27 @@ __device__ __forceinline__ void combine_row(const Args& a, int b, int i, int64_t
     }
     if (SAMPLED) {
         double* pref = a.prefp + row * (NC + 1);
-        if (lane < NC) pref[lane + 1] = incl;
-        if (lane == 0) pref[0] = 0.0;
+        if (lane < NC) put_f64(&pref[lane + 1], incl);
+        if (lane == 0) put_f64(&pref[0], 0.0);
     }
     if (lane == 0) {
         const int t = i < K ? a.dt[(int64_t)b * K + i] : -1;
         const bool tin = t >= 0 && t < V;
         const float pt = (i < K && tin) ? a.tp[row * V + t] : 0.0f;
         const float qt = (pair && tin) ? a.dp[((int64_t)b * K + i) * V + t] : 0.0f;
-        RowRes rr{};
-        rr.P = P;
-        rr.Q = Q;
-        rr.Smin = Smin;
-        rr.W = 0.0;
-        rr.maxv = mv;
-        rr.pt = pt;
-        rr.qt = qt;
-        rr.arg = ai;
+        int acc = 1, draw = SAMPLED ? 1 : 0;
         if (pair) {
             const double ui = (double)a.u[(int64_t)b * (K + 1) + i];
-            rr.acc = (ui * (double)qt * P < (double)pt * Q) ? 1 : 0;
-            rr.draw = rr.acc ? 0 : 1;
-        } else {
-            rr.acc = 1;
-            rr.draw = SAMPLED ? 1 : 0;
+            acc = (ui * (double)qt * P < (double)pt * Q) ? 1 : 0;
+            draw = acc ? 0 : 1;
         }
-        rr.cand = -1;
-        a.rowres[row] = rr;
+        RowRes* rr = &a.rowres[row];
+        put_f64(&rr->P, P);
+        put_f64(&rr->Q, Q);
+        put_i32(&rr->arg, ai);
+        put_i32(&rr->acc, acc);
+        put_i32(&rr->draw, draw);
+        put_i32(&rr->cand, -1);
         if (a.stats) {
             sv_row_stats s;
             s.argmax = ai;
@@ -410,8 +444,9 @@ __device__ __forceinline__ void combine_row(const Args& a, int b, int i, int64_t
             s.q_t = qt;
             a.stats[row] = s;
         }
-        a.cnt1[row] = 0u;                     // nobody else touches it this launch
-        if (SAMPLED) store_release(&a.flag1[row], 1u);
+        put_u32(&a.cnt1[row], 0u);           // nobody else touches it this launch
+        publish();
+        if (SAMPLED) put_u32(&a.flag1[row], 1u);
     }
 }
 
@@ -420,17 +455,16 @@ __device__ __forceinline__ void combine_residual(const Args& a, int64_t row)
 {
     const int lane = threadIdx.x & 63;
     const int NC = a.NC;
-    fence_acquire();
-    const double v = lane < NC ? a.wpart[row * NC + lane] : 0.0;
+    observe();
+    const double v = lane < NC ? get_f64(&a.wpart[row * NC + lane]) : 0.0;
     const double incl = wave_inclusive_scan(v);
-    const double W = __shfl(incl, NC - 1);
     double* pref = a.prefw + row * (NC + 1);
-    if (lane < NC) pref[lane + 1] = incl;
+    if (lane < NC) put_f64(&pref[lane + 1], incl);   // pref[NC] is the residual mass W
     if (lane == 0) {
-        pref[0] = 0.0;
-        a.rowres[row].W = W;
-        a.cnt2[row] = 0u;
-        store_release(&a.flag2[row], 1u);
+        put_f64(&pref[0], 0.0);
+        put_u32(&a.cnt2[row], 0u);
+        publish();
+        put_u32(&a.flag2[row], 1u);
     }
 }
 
@@ -559,12 +593,12 @@ __device__ __forceinline__ void resolve_greedy(const Args& a, int b)
     const int lane = threadIdx.x & 63;
     const int K = a.K;
     const int64_t r0 = (int64_t)b * (K + 1);
-    fence_acquire();
+    observe();
     int n = K;
     for (int base = 0; base < K; base += 64) {
         const int i = base + lane;
         bool miss = false;
-        if (i < K) miss = a.dt[(int64_t)b * K + i] != a.rowres[r0 + i].arg;
+        if (i < K) miss = a.dt[(int64_t)b * K + i] != get_i32(&a.rowres[r0 + i].arg);
         const unsigned long long m = __ballot(miss);
         if (m) {
             n = base + __ffsll((unsigned long long)m) - 1;
@@ -572,12 +606,12 @@ __device__ __forceinline__ void resolve_greedy(const Args& a, int b)
         }
     }
     int next = 0;
-    if (lane == 0) next = a.rowres[r0 + n].arg;
+    if (lane == 0) next = get_i32(&a.rowres[r0 + n].arg);
     next = __shfl(next, 0);   // the load has completed before any lane zeroes the row results
     if (lane == 0) {
         a.n_out[b] = n;
         a.next_out[b] = next;
-        a.seqcnt[b] = 0u;
+        put_u32(&a.seqcnt[b], 0u);
     }
     zero_sequence_data(a, b, false);
 }
@@ -587,11 +621,11 @@ __device__ __forceinline__ void resolve_sampled(const Args& a, int b)
     const int lane = threadIdx.x & 63;
     const int K = a.K;
     const int64_t r0 = (int64_t)b * (K + 1);
-    fence_acquire();
+    observe();
     int n = K;
     for (int base = 0; base < K; base += 64) {
         const int i = base + lane;
-        const bool rej = i < K && a.rowres[r0 + i].acc == 0;
+        const bool rej = i < K && get_i32(&a.rowres[r0 + i].acc) == 0;
         const unsigned long long m = __ballot(rej);
         if (m) {
             n = base + __ffsll((unsigned long long)m) - 1;
@@ -599,16 +633,16 @@ __device__ __forceinline__ void resolve_sampled(const Args& a, int b)
         }
     }
     int next = 0;
-    if (lane == 0) next = a.rowres[r0 + n].cand;
+    if (lane == 0) next = get_i32(&a.rowres[r0 + n].cand);
     next = __shfl(next, 0);   // the load has completed before any lane zeroes the row results
     if (lane == 0) {
         a.n_out[b] = n;
         a.next_out[b] = next;
-        a.seqcnt[b] = 0u;
+        put_u32(&a.seqcnt[b], 0u);
     }
     for (int i = lane; i <= K; i += 64) {
-        a.flag1[r0 + i] = 0u;
-        a.flag2[r0 + i] = 0u;
+        put_u32(&a.flag1[r0 + i], 0u);
+        put_u32(&a.flag2[r0 + i], 0u);
     }
     zero_sequence_data(a, b, true);
 }
@@ -633,14 +667,21 @@ __global__ __launch_bounds__(kThreads) void sv_greedy_kernel(Args a)
     const Acc t = thread_stats<false>(pv, pv, a.V, c);
     const Acc s = block_reduce<false>(t);
     if (threadIdx.x == 0) {
-        a.parts[row * NC + c] = ChunkPart{s.sp, 0.0, 0.0, s.maxv, s.arg};
-        s_last = add_acq_rel(&a.cnt1[row], 1u) == (unsigned)NC - 1u;
+        ChunkPart* dst = &a.parts[row * NC + c];
+        put_f64(&dst->sp, s.sp);
+        put_f32(&dst->maxv, s.maxv);
+        put_i32(&dst->arg, s.arg);
+        publish();
+        s_last = count_up(&a.cnt1[row]) == (unsigned)NC - 1u;
     }
     __syncthreads();
     if (!s_last || threadIdx.x >= 64) return;
     combine_row<false>(a, b, i, row);
     int last_row = 0;
-    if (threadIdx.x == 0) last_row = add_acq_rel(&a.seqcnt[b], 1u) == (unsigned)K;
+    if (threadIdx.x == 0) {
+        publish();
+        last_row = count_up(&a.seqcnt[b]) == (unsigned)K;
+    }
     last_row = __shfl(last_row, 0);
     if (last_row) resolve_greedy(a, b);
 }
@@ -669,8 +710,16 @@ __device__ __forceinline__ void sample_item(const Args& a, int b, int i, int c)
 
     // rendezvous 1: row masses, argmax, acceptance
     if (threadIdx.x == 0) {
-        a.parts[row * NC + c] = ChunkPart{s.sp, s.sq, s.smin, s.maxv, s.arg};
-        s_last = add_acq_rel(&a.cnt1[row], 1u) == (unsigned)NC - 1u;
+        ChunkPart* dst = &a.parts[row * NC + c];
+        put_f64(&dst->sp, s.sp);
+        if (pair) {
+            put_f64(&dst->sq, s.sq);
+            put_f64(&dst->smin, s.smin);
+        }
+        put_f32(&dst->maxv, s.maxv);
+        put_i32(&dst->arg, s.arg);
+        publish();
+        s_last = count_up(&a.cnt1[row]) == (unsigned)NC - 1u;
     }
     __syncthreads();
     if (s_last) {
@@ -681,9 +730,9 @@ __device__ __forceinline__ void sample_item(const Args& a, int b, int i, int c)
     __syncthreads();
     if (threadIdx.x == 0) {
         const RowRes* rr = &a.rowres[row];
-        s_P = rr->P;
-        s_Q = rr->Q;
-        s_draw = rr->draw;
+        s_P = get_f64(&rr->P);
+        s_Q = get_f64(&rr->Q);
+        s_draw = get_i32(&rr->draw);
     }
     __syncthreads();
     const double P = s_P, Q = s_Q;
@@ -703,8 +752,9 @@ __device__ __forceinline__ void sample_item(const Args& a, int b, int i, int c)
             }
             wsum = block_sum(wsum);
             if (threadIdx.x == 0) {
-                a.wpart[row * NC + c] = wsum;
-                s_last = add_acq_rel(&a.cnt2[row], 1u) == (unsigned)NC - 1u;
+                put_f64(&a.wpart[row * NC + c], wsum);
+                publish();
+                s_last = count_up(&a.cnt2[row]) == (unsigned)NC - 1u;
             }
             __syncthreads();
             if (s_last) {
@@ -719,7 +769,7 @@ __device__ __forceinline__ void sample_item(const Args& a, int b, int i, int c)
             double mass = P;
             int resid = 0;
             if (pair) {
-                const double W = a.prefw[row * (NC + 1) + NC];
+                const double W = get_f64(&a.prefw[row * (NC + 1) + NC]);
                 if (W > 0.0) {
                     pref = a.prefw + row * (NC + 1);
                     mass = W;
@@ -727,7 +777,7 @@ __device__ __forceinline__ void sample_item(const Args& a, int b, int i, int c)
                 }
             }
             const double T = uK * mass;
-            const double lo = pref[c], hi = pref[c + 1];
+            const double lo = get_f64(&pref[c]), hi = get_f64(&pref[c + 1]);
             s_owner = (lo <= T && T < hi) ? 1 : 0;
             s_resid = resid;
             s_T = T;
@@ -737,14 +787,15 @@ __device__ __forceinline__ void sample_item(const Args& a, int b, int i, int c)
         if (s_owner) {
             const int x = s_resid ? chunk_draw<true>(pv, qv, P, Q, c, s_lo, s_T)
                                   : chunk_draw<false>(pv, qv, P, Q, c, s_lo, s_T);
-            if (threadIdx.x == 0) a.rowres[row].cand = x;
+            if (threadIdx.x == 0) put_i32(&a.rowres[row].cand, x);
         }
     }
 
     // sequence completion
     if (threadIdx.x == 0) {
         const unsigned per_seq = (unsigned)(K + 1) * (unsigned)NC;
-        s_last = add_acq_rel(&a.seqcnt[b], 1u) == per_seq - 1u;
+        publish();
+        s_last = count_up(&a.seqcnt[b]) == per_seq - 1u;
     }
     __syncthreads();
     if (s_last && threadIdx.x < 64) resolve_sampled(a, b);
@@ -757,7 +808,7 @@ __global__ __launch_bounds__(kThreads, 2) void sv_sample_kernel(Args a)
     __shared__ unsigned s_ticket;
     const unsigned per_seq = (unsigned)(a.K + 1) * (unsigned)a.NC;
     for (;;) {
-        if (threadIdx.x == 0) s_ticket = add_acq_rel(&a.hdr->ticket, 1u);
+        if (threadIdx.x == 0) s_ticket = count_up(&a.hdr->ticket);   // carries no data
         __syncthreads();
         const unsigned tk = s_ticket;
         __syncthreads();
@@ -769,9 +820,9 @@ __global__ __launch_bounds__(kThreads, 2) void sv_sample_kernel(Args a)
         sample_item<VEC>(a, b, i, c);
     }
     if (threadIdx.x == 0) {
-        if (add_acq_rel(&a.hdr->exit_count, 1u) == gridDim.x - 1u) {
-            a.hdr->ticket = 0u;     // every block has taken its last ticket
-            a.hdr->exit_count = 0u;
+        if (count_up(&a.hdr->exit_count) == gridDim.x - 1u) {
+            put_u32(&a.hdr->ticket, 0u);     // every block has taken its last ticket
+            put_u32(&a.hdr->exit_count, 0u);
         }
     }
 }
