@@ -8,30 +8,32 @@
 //
 // Work decomposition (the vocabulary axis is the long one):
 //   * every row of V values is cut into NC = ceil(V / 8192) chunks; a
-//     256-thread block (4 waves) owns one chunk of one row; each thread loads
-//     8 float4 per operand (coalesced 16-byte loads, 32 KB per operand per
-//     block) and keeps them in VGPRs;
-//   * per-chunk partials (fp64 masses, lowest-index argmax) are combined per
-//     row by the last block to arrive (agent-scope acq_rel ticket), always in
-//     the same lane order, so every result depends on V alone, never on B, K,
-//     the launch shape or timing;
-//   * greedy needs nothing more: the last row of a sequence to complete
-//     resolves (n_accepted, next_token);
-//   * sampled runs persistently with atomic work tickets handed out in
-//     (sequence, row, chunk) order.  After its row has been combined every
-//     block of a rejecting row computes its chunk's residual mass from the
-//     values still in registers; after a second row-level rendezvous the one
-//     block whose chunk holds u_K * W runs the inverse-CDF search in
-//     registers.  The bonus row works the same way on the mass partials.  No
-//     row is read twice from HBM.
+//     256-thread block (4 waves) streams one chunk of one row (and, in
+//     sampled mode, the same chunk of the matching draft row): each thread
+//     issues 8 coalesced, non-temporal 16-byte loads per operand;
+//   * per-chunk partials (fp64 masses, lowest-index argmax) are combined in
+//     lane (= chunk) order by the last block of the row to arrive, so every
+//     result depends on V alone, never on B, K, the launch shape or timing;
+//   * the last row of a sequence to complete resolves the accept-prefix
+//     length n (the first rejected draft, or K);
+//   * greedy: next token = argmax of row n; no block ever waits.
+//   * sampled: a persistent grid takes work tickets in order.  Row tickets
+//     (pass 1) never wait.  For each sequence b, NC residual tickets follow
+//     kLag sequences later in the ticket order; by then b is normally
+//     resolved and its rows were streamed moments ago, so the residual
+//     re-read of the rejected pair (p_n, q_n) is served by the Infinity Cache
+//     rather than HBM.  Each residual ticket adds its chunk's mass of
+//     w = max(0, p_n*Q - q_n*P); the last one combines them and the block
+//     whose chunk holds u_K * W runs the inverse-CDF search over that chunk.
+//     When every draft is accepted, the resolver draws the bonus token from
+//     p_K the same way (chunk masses of p_K locate the chunk), and the
+//     sequence's residual tickets do nothing but count.
 //
-// Deadlock freedom of the row rendezvous: tickets are taken in order, so all
-// rows except the one holding the newest ticket have every chunk taken, and
-// their blocks reach the rendezvous without waiting.  A block waits only on
-// its own row, so at most NC - 1 blocks wait on the one incomplete row; the
-// host launches at least NC resident blocks, so some block always advances.
-// Every wait is also bounded (it raises the workspace fault word instead of
-// spinning forever).
+// Progress: the only wait is a residual ticket whose sequence is not yet
+// resolved.  All of that sequence's row tickets come earlier in the ticket
+// order, so they are held by running blocks, and row tickets never wait:
+// the sequence resolves.  The wait is also bounded in time (expiry raises
+// the workspace fault word instead of spinning forever).
 
 #include <hip/hip_runtime.h>
 
@@ -53,7 +55,8 @@ constexpr int kChunk4 = kThreads * kVec;       // float4 per chunk
 constexpr int kChunk = kChunk4 * 4;            // 8192 values per chunk
 constexpr int kMaxChunks = 64;                 // one chunk per lane of a wave
 static_assert(SV_MAX_V == kMaxChunks * kChunk, "SV_MAX_V must match the chunk geometry");
-constexpr double kWaitSeconds = 2.0;           // bound of every cross-block wait
+constexpr int kLag = 16;                       // residual tickets trail their sequence
+constexpr double kWaitSeconds = 2.0;           // bound of the one cross-block wait
 
 struct Header {              // 256 bytes
     unsigned ticket;         // next work ticket (sampled)
@@ -68,15 +71,19 @@ struct ChunkPart {           // 32 bytes
     int arg;
 };
 
-struct RowRes {              // 64 bytes
-    double P, Q, Smin, W;
-    float maxv, pt, qt;
-    int arg;
-    int acc, draw, cand, pad;
+struct RowRes {              // 32 bytes
+    double P, Q;             // row masses
+    int acc, arg;            // acceptance bit of the row's draft, lowest-index argmax
+    int pad[2];
+};
+
+struct SeqInfo {             // 8 bytes
+    int n;                   // accept-prefix length
+    unsigned resolved;       // 1 once n is published
 };
 
 struct Layout {
-    size_t hdr, cnt1, cnt2, flag1, flag2, seqcnt, rowres, parts, wpart, prefp, prefw, total;
+    size_t hdr, cnt1, cnt2, seqcnt, seqinfo, rowres, parts, wpart, zero, total;
 };
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -86,17 +93,15 @@ inline Layout make_layout(int64_t B, int64_t K, int64_t NC)
     const size_t R = (size_t)(B * (K + 1));
     Layout L{};
     size_t o = 0;
-    L.hdr = o;    o = align_up(o + sizeof(Header), 256);
-    L.cnt1 = o;   o = align_up(o + R * 4, 256);
-    L.cnt2 = o;   o = align_up(o + R * 4, 256);
-    L.flag1 = o;  o = align_up(o + R * 4, 256);
-    L.flag2 = o;  o = align_up(o + R * 4, 256);
-    L.seqcnt = o; o = align_up(o + (size_t)B * 4, 256);
-    L.rowres = o; o = align_up(o + R * sizeof(RowRes), 256);
-    L.parts = o;  o = align_up(o + R * (size_t)NC * sizeof(ChunkPart), 256);
-    L.wpart = o;  o = align_up(o + R * (size_t)NC * 8, 256);
-    L.prefp = o;  o = align_up(o + R * (size_t)(NC + 1) * 8, 256);
-    L.prefw = o;  o = align_up(o + R * (size_t)(NC + 1) * 8, 256);
+    L.hdr = o;     o = align_up(o + sizeof(Header), 256);
+    L.cnt1 = o;    o = align_up(o + R * 4, 256);
+    L.cnt2 = o;    o = align_up(o + (size_t)B * 4, 256);
+    L.seqcnt = o;  o = align_up(o + (size_t)B * 4, 256);
+    L.seqinfo = o; o = align_up(o + (size_t)B * sizeof(SeqInfo), 256);
+    L.rowres = o;  o = align_up(o + R * sizeof(RowRes), 256);
+    L.parts = o;   o = align_up(o + R * (size_t)NC * sizeof(ChunkPart), 256);
+    L.wpart = o;   o = align_up(o + (size_t)B * (size_t)NC * 8, 256);
+    L.zero = o;    o = align_up(o + (size_t)kChunk * 4, 256);   // never written
     L.total = o;
     return L;
 }
@@ -110,25 +115,26 @@ struct Args {
     int32_t* next_out;
     sv_row_stats* stats;
     Header* hdr;
-    unsigned *cnt1, *cnt2, *flag1, *flag2, *seqcnt;
+    unsigned *cnt1, *cnt2, *seqcnt;
+    SeqInfo* seqinfo;
     RowRes* rowres;
     ChunkPart* parts;
     double* wpart;
-    double* prefp;
-    double* prefw;
+    const float* zero;       // one chunk of zeros (the bonus row's draft operand)
     int B, K, V, NC;
-    unsigned total;          // work items (sampled)
+    int lag;                 // min(kLag, B)
+    unsigned total;          // work tickets (sampled)
     unsigned long long wait_ticks;   // wait bound in wall-clock ticks
 };
 
 // ------------------------------------------- cross-block communication --
 //
 // Every value one block publishes for another (chunk partials, row results,
-// prefixes, counters, flags) is written and read with agent-scope atomic
-// accesses.  On gfx950 these are performed at the device-coherent level
-// (sc1 loads and stores; RMW atomics at the memory side) instead of in the
-// per-XCD L2, so no L2 write-back or invalidate (the cost of agent-scope
-// release/acquire fences) is ever needed.  Ordering is explicit:
+// counters) is written and read with agent-scope atomic accesses.  On gfx950
+// these are performed at the device-coherent level (sc1 loads and stores;
+// RMW atomics at the memory side) instead of in the per-XCD L2, so no L2
+// write-back or invalidate (the cost of agent-scope release/acquire fences)
+// is ever needed.  Ordering is explicit:
 //   writer: data stores -> publish() -> counter RMW or flag store
 //   reader: counter RMW or flag load -> observe() -> data loads
 // publish() waits for the wave's outstanding memory operations to complete
@@ -171,13 +177,13 @@ __device__ __forceinline__ double get_f64(const double* p)
     return __longlong_as_double((long long)get_u64(p));
 }
 
-// Bounded wait for a row flag; on expiry raises the fault word and returns
-// (the call's outputs are then unspecified, but every block still exits).
+// Bounded wait until *flag != 0; on expiry raises the fault word and returns
+// (the call's outputs are then unspecified, but every block exits).
 __device__ __forceinline__ void wait_flag(const unsigned* flag, Header* hdr, unsigned long long ticks)
 {
     const unsigned long long t0 = wall_clock64();
     while (get_u32(flag) == 0u) {
-        __builtin_amdgcn_s_sleep(2);
+        __builtin_amdgcn_s_sleep(8);
         if (wall_clock64() - t0 > ticks) {
             put_u32(&hdr->error, 1u);
             break;
@@ -194,18 +200,20 @@ __device__ __forceinline__ void wave_zero(void* p, size_t bytes)
     for (size_t j = threadIdx.x & 63; j < n; j += 64) put_u64(q + j, 0ull);
 }
 
-// Once sequence b is resolved nothing reads its partials, prefixes or row
+// Once sequence b is finished nothing reads its counters, partials or row
 // results again: return them to zero so that the whole workspace is zero
-// between calls, whatever shapes the next call uses.
-__device__ __forceinline__ void zero_sequence_data(const Args& a, int b, bool sampled)
+// between calls, whatever shapes the next call uses.  One wave calls it.
+__device__ __forceinline__ void zero_sequence(const Args& a, int b)
 {
     const int64_t rows = a.K + 1, r0 = (int64_t)b * rows, NC = a.NC;
     wave_zero(a.parts + r0 * NC, (size_t)(rows * NC) * sizeof(ChunkPart));
     wave_zero(a.rowres + r0, (size_t)rows * sizeof(RowRes));
-    if (sampled) {
-        wave_zero(a.wpart + r0 * NC, (size_t)(rows * NC) * 8);
-        wave_zero(a.prefp + r0 * (NC + 1), (size_t)(rows * (NC + 1)) * 8);
-        wave_zero(a.prefw + r0 * (NC + 1), (size_t)(rows * (NC + 1)) * 8);
+    wave_zero(a.wpart + (int64_t)b * NC, (size_t)NC * 8);
+    for (int64_t j = threadIdx.x & 63; j < rows; j += 64) put_u32(&a.cnt1[r0 + j], 0u);
+    if ((threadIdx.x & 63) == 0) {
+        put_u32(&a.cnt2[b], 0u);
+        put_u32(&a.seqcnt[b], 0u);
+        put_u64(&a.seqinfo[b], 0ull);
     }
 }
 
@@ -215,7 +223,23 @@ __device__ __forceinline__ void zero_sequence_data(const Args& a, int b, bool sa
 // consecutive threads read consecutive 16-byte words (fully coalesced).
 __device__ __forceinline__ int f4_index(int c, int k) { return c * kChunk4 + k * kThreads + (int)threadIdx.x; }
 
-template <bool VEC>
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Streaming load: every value is read once, so it is not kept in cache.
+__device__ __forceinline__ float4 load_stream(const float4* p)
+{
+    const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    return make_float4(t.x, t.y, t.z, t.w);
+}
+__device__ __forceinline__ float load_stream(const float* p) { return __builtin_nontemporal_load(p); }
+
+// Loads of float4 numbers k in [0, kVec) of chunk c.  Every load is
+// unconditional (an out-of-range index is clamped to the row's last element)
+// and nothing is written to the destination registers afterwards: values
+// past the row's end are masked where they are consumed (thread_stats), so
+// all loads of a thread are in flight together.  STREAM selects the
+// non-temporal hint (first pass) or ordinary cached loads.
+template <bool VEC, bool STREAM>
 __device__ __forceinline__ void load_chunk(const float* __restrict__ row, int V, int c, float4 (&v)[kVec])
 {
     if constexpr (VEC) {
@@ -224,35 +248,53 @@ __device__ __forceinline__ void load_chunk(const float* __restrict__ row, int V,
 #pragma unroll
         for (int k = 0; k < kVec; ++k) {
             const int f = f4_index(c, k);
-            v[k] = f < nf ? r4[f] : make_float4(0.f, 0.f, 0.f, 0.f);
+            const float4* src = r4 + (f < nf ? f : nf - 1);
+            v[k] = STREAM ? load_stream(src) : *src;
         }
     } else {
 #pragma unroll
         for (int k = 0; k < kVec; ++k) {
             const int x = f4_index(c, k) * 4;
-            v[k].x = x + 0 < V ? row[x + 0] : 0.f;
-            v[k].y = x + 1 < V ? row[x + 1] : 0.f;
-            v[k].z = x + 2 < V ? row[x + 2] : 0.f;
-            v[k].w = x + 3 < V ? row[x + 3] : 0.f;
+            float e[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float* src = row + (x + j < V ? x + j : V - 1);
+                e[j] = STREAM ? load_stream(src) : *src;
+            }
+            v[k] = make_float4(e[0], e[1], e[2], e[3]);
         }
     }
 }
 
-// Opaque to the optimiser: forces later phases to reconvert the f32 values
-// kept in registers instead of keeping fp64 copies of all of them alive.
-__device__ __forceinline__ void reg_barrier(float4 (&v)[kVec])
+// Cached load of float4 number k (runtime) of chunk c, zero outside the row.
+template <bool VEC>
+__device__ __forceinline__ float4 load_one(const float* __restrict__ row, int V, int c, int k)
 {
+    if constexpr (VEC) {
+        const float4* r4 = reinterpret_cast<const float4*>(row);
+        const int nf = V >> 2, f = f4_index(c, k);
+        const float4 v = r4[f < nf ? f : nf - 1];
+        return f < nf ? v : make_float4(0.f, 0.f, 0.f, 0.f);
+    } else {
+        const int x = f4_index(c, k) * 4;
+        float e[4];
 #pragma unroll
-    for (int k = 0; k < kVec; ++k) {
-        float x = v[k].x, y = v[k].y, z = v[k].z, w = v[k].w;
-        asm volatile("" : "+v"(x), "+v"(y), "+v"(z), "+v"(w));
-        v[k] = make_float4(x, y, z, w);
+        for (int j = 0; j < 4; ++j) e[j] = row[x + j < V ? x + j : V - 1];
+        return make_float4(x + 0 < V ? e[0] : 0.f, x + 1 < V ? e[1] : 0.f,
+                           x + 2 < V ? e[2] : 0.f, x + 3 < V ? e[3] : 0.f);
     }
 }
 
 __device__ __forceinline__ float comp(float4 v, int e)
 {
     return e == 0 ? v.x : (e == 1 ? v.y : (e == 2 ? v.z : v.w));
+}
+
+// Residual mass of one value: max(0, p*Q - q*P), fp64, no contraction.
+__device__ __forceinline__ double resid(float p, float q, double P, double Q)
+{
+    const double d = (double)p * Q - (double)q * P;
+    return d > 0.0 ? d : 0.0;
 }
 
 // ------------------------------------------------------- reductions --
@@ -273,6 +315,8 @@ __device__ __forceinline__ void argmax_merge(float& v, int& i, float ov, int oi)
     }
 }
 
+// Per-thread partials of one chunk as load_chunk left it: values at index
+// V or beyond (clamped duplicates) are masked to 0 here.
 template <bool PAIR>
 __device__ __forceinline__ Acc thread_stats(const float4 (&pv)[kVec], const float4 (&qv)[kVec], int V, int c)
 {
@@ -282,18 +326,20 @@ __device__ __forceinline__ Acc thread_stats(const float4 (&pv)[kVec], const floa
         const int x0 = f4_index(c, k) * 4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const float p = comp(pv[k], e);
-            if (x0 + e < V && p > a.maxv) {
+            const bool in = x0 + e < V;
+            const float p = in ? comp(pv[k], e) : 0.0f;
+            if (in && p > a.maxv) {
                 a.maxv = p;
                 a.arg = x0 + e;
             }
-            a.sp += (double)p;                       // padding values are 0
+            a.sp += (double)p;
             if constexpr (PAIR) {
-                const float q = comp(qv[k], e);
+                const float q = in ? comp(qv[k], e) : 0.0f;
                 a.sq += (double)q;
                 a.smin += (double)fminf(p, q);
             }
         }
+        __builtin_amdgcn_sched_barrier(0);   // keep fp64 temporaries to one float4 at a time
     }
     return a;
 }
@@ -372,112 +418,82 @@ __device__ __forceinline__ double block_sum(double v)
 
 // ------------------------------------------------------ row combine --
 
-// Wave 0 of the block that completed a row: combine the NC chunk partials in
-// lane (= chunk) order, publish the row result, the prefix of the chunk mass
-// partials and, when `stats` is set, the row statistics; then release the
-// row flag (sampled) so the other chunks of the row may proceed.
-template <bool SAMPLED>
-__device__ __forceinline__ void combine_row(const Args& a, int b, int i, int64_t row)
+struct RowView {
+    double P, Q, Smin;       // row masses
+    float maxv;
+    int arg;
+};
+
+// Wave-cooperative (all 64 lanes of one wave): combine the NC chunk partials
+// of a row in lane (= chunk) order.
+template <bool PAIR>
+__device__ __forceinline__ RowView combine_row(const ChunkPart* parts, int NC)
 {
     const int lane = threadIdx.x & 63;
-    const int NC = a.NC, K = a.K, V = a.V;
-    const bool pair = SAMPLED && i < K;
     observe();
-    ChunkPart cp{0.0, 0.0, 0.0, -INFINITY, INT_MAX};
+    double sp = 0.0, sq = 0.0, sm = 0.0;
+    float mv = -INFINITY;
+    int ai = INT_MAX;
     if (lane < NC) {
-        const ChunkPart* src = &a.parts[row * NC + lane];
-        cp.sp = get_f64(&src->sp);
-        if (pair) {
-            cp.sq = get_f64(&src->sq);
-            cp.smin = get_f64(&src->smin);
+        sp = get_f64(&parts[lane].sp);
+        if constexpr (PAIR) {
+            sq = get_f64(&parts[lane].sq);
+            sm = get_f64(&parts[lane].smin);
         }
-        cp.maxv = get_f32(&src->maxv);
-        cp.arg = get_i32(&src->arg);
+        mv = get_f32(&parts[lane].maxv);
+        ai = get_i32(&parts[lane].arg);
     }
-    float mv = cp.maxv;
-    int ai = cp.arg;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
         const float ov = __shfl_xor(mv, off);
         const int oi = __shfl_xor(ai, off);
         argmax_merge(mv, ai, ov, oi);
     }
-    const double incl = wave_inclusive_scan(cp.sp);
-    const double P = __shfl(incl, NC - 1);
-    double Q = 0.0, Smin = 0.0;
-    if (pair) {
-        Q = wave_sum(cp.sq);
-        Smin = wave_sum(cp.smin);
-    }
-    if (SAMPLED) {
-        double* pref = a.prefp + row * (NC + 1);
-        if (lane < NC) put_f64(&pref[lane + 1], incl);
-        if (lane == 0) put_f64(&pref[0], 0.0);
-    }
-    if (lane == 0) {
-        const int t = i < K ? a.dt[(int64_t)b * K + i] : -1;
-        const bool tin = t >= 0 && t < V;
-        const float pt = (i < K && tin) ? a.tp[row * V + t] : 0.0f;
-        const float qt = (pair && tin) ? a.dp[((int64_t)b * K + i) * V + t] : 0.0f;
-        int acc = 1, draw = SAMPLED ? 1 : 0;
-        if (pair) {
-            const double ui = (double)a.u[(int64_t)b * (K + 1) + i];
-            acc = (ui * (double)qt * P < (double)pt * Q) ? 1 : 0;
-            draw = acc ? 0 : 1;
-        }
-        RowRes* rr = &a.rowres[row];
-        put_f64(&rr->P, P);
-        put_f64(&rr->Q, Q);
-        put_i32(&rr->arg, ai);
-        put_i32(&rr->acc, acc);
-        put_i32(&rr->draw, draw);
-        put_i32(&rr->cand, -1);
-        if (a.stats) {
-            sv_row_stats s;
-            s.argmax = ai;
-            s.max_p = mv;
-            s.sum_p = P;
-            s.sum_q = Q;
-            s.sum_min = Smin;
-            s.sum_pos = pair ? P - Smin : 0.0;
-            s.p_t = pt;
-            s.q_t = qt;
-            a.stats[row] = s;
-        }
-        put_u32(&a.cnt1[row], 0u);           // nobody else touches it this launch
-        publish();
-        if (SAMPLED) put_u32(&a.flag1[row], 1u);
-    }
+    const double incl = wave_inclusive_scan(sp);
+    RowView r;
+    r.P = __shfl(incl, NC - 1);
+    r.Q = PAIR ? wave_sum(sq) : 0.0;
+    r.Smin = PAIR ? wave_sum(sm) : 0.0;
+    r.maxv = mv;
+    r.arg = ai;
+    return r;
 }
 
-// Wave 0 of the block that completed the residual partials of a row.
-__device__ __forceinline__ void combine_residual(const Args& a, int64_t row)
+// Wave-cooperative: given the NC chunk masses m[c] (lane c), the chunk that
+// holds T = u * (total) -- the one with prefix(c-1) <= T < prefix(c) -- and
+// its base prefix(c-1).  Prefixes are the inclusive scan in lane order; the
+// total is its last entry, so T < total always has an owner when total > 0.
+// Returns the total; *owner = -1 when no chunk qualifies (total == 0).
+__device__ __forceinline__ double locate_chunk(double m, int NC, double u, int* owner, double* base,
+                                               double* T_out)
 {
     const int lane = threadIdx.x & 63;
-    const int NC = a.NC;
-    observe();
-    const double v = lane < NC ? get_f64(&a.wpart[row * NC + lane]) : 0.0;
-    const double incl = wave_inclusive_scan(v);
-    double* pref = a.prefw + row * (NC + 1);
-    if (lane < NC) put_f64(&pref[lane + 1], incl);   // pref[NC] is the residual mass W
-    if (lane == 0) {
-        put_f64(&pref[0], 0.0);
-        put_u32(&a.cnt2[row], 0u);
-        publish();
-        put_u32(&a.flag2[row], 1u);
-    }
+    const double incl = wave_inclusive_scan(lane < NC ? m : 0.0);
+    const double total = __shfl(incl, NC - 1);
+    const double T = u * total;
+    double lo = __shfl_up(incl, 1);
+    if (lane == 0) lo = 0.0;
+    const bool own = lane < NC && lo <= T && T < incl;
+    const unsigned long long mk = __ballot(own);
+    const int c = mk ? __ffsll((unsigned long long)mk) - 1 : -1;
+    *owner = c;
+    *base = c >= 0 ? __shfl(lo, c) : 0.0;
+    *T_out = T;
+    return total;
 }
 
 // ---------------------------------------------------- inverse CDF --
 
-// Search of this block's chunk for the smallest x with
+// Search of chunk c for the smallest x with
 // base + sum_{chunk start <= y <= x} w(y) > T, where w is the residual
 // max(0, p*Q - q*P) (RESID) or p itself.  If rounding leaves no such x in
-// the chunk, the last x with w(x) > 0 is taken.  All threads must call; the
-// token is returned in every thread.
-template <bool RESID>
-__device__ __forceinline__ int chunk_draw(const float4 (&pv)[kVec], const float4 (&qv)[kVec], double P, double Q,
-                          int c, double base, double T)
+// the chunk, the last x with w(x) > 0 is taken.  The chunk is re-read with
+// cached loads a few float4s per thread at a time, and the selected segment
+// once more for the final scan (few registers; a rare path).  All threads of
+// the block must call; the token is returned in every thread.
+template <bool VEC, bool RESID>
+__device__ __noinline__ int chunk_draw(const float* prow, const float* qrow, int V, double P, double Q,
+                                       int c, double base, double T)
 {
     __shared__ double s_seg[kVec][kWaves];
     __shared__ int s_ks, s_ws;
@@ -485,29 +501,20 @@ __device__ __forceinline__ int chunk_draw(const float4 (&pv)[kVec], const float4
     __shared__ int s_x;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 
-    auto wval = [&](float4 p4, float4 q4, int e) -> double {
-        const double p = (double)comp(p4, e);
-        if constexpr (RESID) {
-            const double d = p * Q - (double)comp(q4, e) * P;
-            return d > 0.0 ? d : 0.0;
-        } else {
-            (void)q4;
-            return p;
-        }
+    auto wsum4 = [&](float4 p4, float4 q4) -> double {   // one float4, in index order
+        double t = 0.0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            t += RESID ? resid(comp(p4, e), comp(q4, e), P, Q) : (double)comp(p4, e);
+        return t;
     };
 
-    double sk[kVec];
-#pragma unroll
-    for (int k = 0; k < kVec; ++k) {
-        double s = 0.0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) s += wval(pv[k], qv[k], e);
-        sk[k] = s;
-    }
     // segment (k, wave) = 256 consecutive values; segments in index order
-#pragma unroll
+#pragma unroll 4
     for (int k = 0; k < kVec; ++k) {
-        const double s = wave_sum(sk[k]);
+        const float4 p4 = load_one<VEC>(prow, V, c, k);
+        const float4 q4 = RESID ? load_one<VEC>(qrow, V, c, k) : p4;
+        const double s = wave_sum(wsum4(p4, q4));
         if (lane == 0) s_seg[k][w] = s;
     }
     __syncthreads();
@@ -541,44 +548,33 @@ __device__ __forceinline__ int chunk_draw(const float4 (&pv)[kVec], const float4
         s_base = bs;
     }
     __syncthreads();
-    const int ks = s_ks;
     if (w == s_ws) {
-        float4 lp[kVec], lq[kVec];
+        const int k = s_ks;
+        const float4 p4 = load_one<VEC>(prow, V, c, k);
+        const float4 q4 = RESID ? load_one<VEC>(qrow, V, c, k) : p4;
+        const double incl = wave_inclusive_scan(wsum4(p4, q4));
+        double run = __shfl_up(incl, 1);
+        if (lane == 0) run = 0.0;
+        run += s_base;
+        int hit = -1, lastpos = -1;
 #pragma unroll
-        for (int k = 0; k < kVec; ++k) {
-            lp[k] = pv[k];
-            lq[k] = qv[k];
+        for (int e = 0; e < 4; ++e) {
+            const double v = RESID ? resid(comp(p4, e), comp(q4, e), P, Q) : (double)comp(p4, e);
+            run += v;
+            if (hit < 0 && run > T) hit = e;
+            if (v > 0.0) lastpos = e;
         }
-        reg_barrier(lp);
-        reg_barrier(lq);
-        // every index below is static: a uniform branch per segment row k
-#pragma unroll
-        for (int k = 0; k < kVec; ++k) {
-            if (k != ks) continue;
-            const double incl = wave_inclusive_scan(sk[k]);
-            double run = __shfl_up(incl, 1);
-            if (lane == 0) run = 0.0;
-            run += s_base;
-            int hit = -1, lastpos = -1;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const double v = wval(lp[k], lq[k], e);
-                run += v;
-                if (hit < 0 && run > T) hit = e;
-                if (v > 0.0) lastpos = e;
-            }
-            const unsigned long long mh = __ballot(hit >= 0);
-            if (mh) {
-                const int l = __ffsll((unsigned long long)mh) - 1;
-                if (lane == l) s_x = f4_index(c, k) * 4 + hit;
-            } else {
-                const unsigned long long mp = __ballot(lastpos >= 0);
-                if (mp) {
-                    const int l = 63 - __clzll(mp);
-                    if (lane == l) s_x = f4_index(c, k) * 4 + lastpos;
-                } else if (lane == 0) {
-                    s_x = f4_index(c, k) * 4;   // unreachable for a segment with mass
-                }
+        const unsigned long long mh = __ballot(hit >= 0);
+        if (mh) {
+            const int l = __ffsll((unsigned long long)mh) - 1;
+            if (lane == l) s_x = f4_index(c, k) * 4 + hit;
+        } else {
+            const unsigned long long mp = __ballot(lastpos >= 0);
+            if (mp) {
+                const int l = 63 - __clzll(mp);
+                if (lane == l) s_x = f4_index(c, k) * 4 + lastpos;
+            } else if (lane == 0) {
+                s_x = f4_index(c, k) * 4;   // unreachable for a segment with mass
             }
         }
     }
@@ -586,19 +582,92 @@ __device__ __forceinline__ int chunk_draw(const float4 (&pv)[kVec], const float4
     return s_x;
 }
 
-// ----------------------------------------------------------- resolve --
-
-__device__ __forceinline__ void resolve_greedy(const Args& a, int b)
+__device__ __forceinline__ void write_stats(const Args& a, int64_t row, const RowView& rv, bool pair,
+                                            float pt, float qt, bool has_t)
 {
-    const int lane = threadIdx.x & 63;
-    const int K = a.K;
+    sv_row_stats s;
+    s.argmax = rv.arg;
+    s.max_p = rv.maxv;
+    s.sum_p = rv.P;
+    s.sum_q = pair ? rv.Q : 0.0;
+    s.sum_min = pair ? rv.Smin : 0.0;
+    s.sum_pos = pair ? rv.P - rv.Smin : 0.0;
+    s.p_t = has_t ? pt : 0.0f;
+    s.q_t = pair ? qt : 0.0f;
+    a.stats[row] = s;
+}
+
+// Wave-cooperative: the accept-prefix length of sequence b from the rows'
+// published acceptance bits.
+__device__ __forceinline__ int first_rejection(const Args& a, int b)
+{
+    const int lane = threadIdx.x & 63, K = a.K;
     const int64_t r0 = (int64_t)b * (K + 1);
-    observe();
     int n = K;
     for (int base = 0; base < K; base += 64) {
         const int i = base + lane;
-        bool miss = false;
-        if (i < K) miss = a.dt[(int64_t)b * K + i] != get_i32(&a.rowres[r0 + i].arg);
+        const bool rej = i < K && get_i32(&a.rowres[r0 + i].acc) == 0;
+        const unsigned long long m = __ballot(rej);
+        if (m) {
+            n = base + __ffsll((unsigned long long)m) - 1;
+            break;
+        }
+    }
+    return n;
+}
+
+// ----------------------------------------------------------- greedy --
+
+template <bool VEC>
+__global__ __launch_bounds__(kThreads) void sv_greedy_kernel(Args a)
+{
+    __shared__ int s_last;
+    const int NC = a.NC, K = a.K, V = a.V;
+    const unsigned per_seq = (unsigned)(K + 1) * (unsigned)NC;
+    const unsigned item = blockIdx.x;
+    const int b = (int)(item / per_seq);
+    const unsigned r = item - (unsigned)b * per_seq;
+    const int i = (int)(r / (unsigned)NC);
+    const int c = (int)(r - (unsigned)i * (unsigned)NC);
+    const int64_t row = (int64_t)b * (K + 1) + i;
+
+    float4 pv[kVec];
+    load_chunk<VEC, true>(a.tp + row * V, V, c, pv);
+    const Acc t = thread_stats<false>(pv, pv, V, c);
+    const Acc s = block_reduce<false>(t);
+    if (threadIdx.x == 0) {
+        ChunkPart* dst = &a.parts[row * NC + c];
+        put_f64(&dst->sp, s.sp);
+        put_f32(&dst->maxv, s.maxv);
+        put_i32(&dst->arg, s.arg);
+        publish();
+        s_last = count_up(&a.cnt1[row]) == (unsigned)NC - 1u;
+    }
+    __syncthreads();
+    if (!s_last || threadIdx.x >= 64) return;
+    // wave 0 of the last block of the row
+    const RowView rv = combine_row<false>(a.parts + row * NC, NC);
+    int last_row = 0;
+    if (threadIdx.x == 0) {
+        put_i32(&a.rowres[row].arg, rv.arg);
+        if (a.stats) {
+            const int tk = i < K ? a.dt[(int64_t)b * K + i] : -1;
+            const bool tin = tk >= 0 && tk < V;
+            write_stats(a, row, rv, false, tin ? a.tp[row * V + tk] : 0.0f, 0.0f, i < K);
+        }
+        publish();
+        last_row = count_up(&a.seqcnt[b]) == (unsigned)K;
+    }
+    last_row = __shfl(last_row, 0);
+    if (!last_row) return;
+    // the sequence's last row: n = first draft that differs from its argmax
+    observe();
+    const int64_t r0 = (int64_t)b * (K + 1);
+    const int lane = threadIdx.x;
+    int n = K;
+    for (int base = 0; base < K; base += 64) {
+        const int j = base + lane;
+        const bool miss = j < K && a.dt[(int64_t)b * K + j] != get_i32(&a.rowres[r0 + j].arg);
         const unsigned long long m = __ballot(miss);
         if (m) {
             n = base + __ffsll((unsigned long long)m) - 1;
@@ -611,213 +680,251 @@ __device__ __forceinline__ void resolve_greedy(const Args& a, int b)
     if (lane == 0) {
         a.n_out[b] = n;
         a.next_out[b] = next;
-        put_u32(&a.seqcnt[b], 0u);
     }
-    zero_sequence_data(a, b, false);
+    zero_sequence(a, b);
 }
 
-__device__ __forceinline__ void resolve_sampled(const Args& a, int b)
-{
-    const int lane = threadIdx.x & 63;
-    const int K = a.K;
-    const int64_t r0 = (int64_t)b * (K + 1);
-    observe();
-    int n = K;
-    for (int base = 0; base < K; base += 64) {
-        const int i = base + lane;
-        const bool rej = i < K && get_i32(&a.rowres[r0 + i].acc) == 0;
-        const unsigned long long m = __ballot(rej);
-        if (m) {
-            n = base + __ffsll((unsigned long long)m) - 1;
-            break;
-        }
-    }
-    int next = 0;
-    if (lane == 0) next = get_i32(&a.rowres[r0 + n].cand);
-    next = __shfl(next, 0);   // the load has completed before any lane zeroes the row results
-    if (lane == 0) {
-        a.n_out[b] = n;
-        a.next_out[b] = next;
-        put_u32(&a.seqcnt[b], 0u);
-    }
-    for (int i = lane; i <= K; i += 64) {
-        put_u32(&a.flag1[r0 + i], 0u);
-        put_u32(&a.flag2[r0 + i], 0u);
-    }
-    zero_sequence_data(a, b, true);
-}
+// ---------------------------------------------------------- sampled --
 
-// ----------------------------------------------------------- kernels --
-
+// Row ticket: chunk c of target row i of sequence b, with the same chunk of
+// draft row i (the zero chunk for the bonus row i == K, so that both kinds
+// run the same straight-line loads).
 template <bool VEC>
-__global__ __launch_bounds__(kThreads) void sv_greedy_kernel(Args a)
+__device__ __forceinline__ void row_item(const Args& a, int b, int i, int c)
 {
-    __shared__ int s_last;
-    const int NC = a.NC, K = a.K;
-    const unsigned per_seq = (unsigned)(K + 1) * (unsigned)NC;
-    const unsigned item = blockIdx.x;
-    const int b = (int)(item / per_seq);
-    const unsigned r = item - (unsigned)b * per_seq;
-    const int i = (int)(r / (unsigned)NC);
-    const int c = (int)(r - (unsigned)i * (unsigned)NC);
-    const int64_t row = (int64_t)b * (K + 1) + i;
-
-    float4 pv[kVec];
-    load_chunk<VEC>(a.tp + row * a.V, a.V, c, pv);
-    const Acc t = thread_stats<false>(pv, pv, a.V, c);
-    const Acc s = block_reduce<false>(t);
-    if (threadIdx.x == 0) {
-        ChunkPart* dst = &a.parts[row * NC + c];
-        put_f64(&dst->sp, s.sp);
-        put_f32(&dst->maxv, s.maxv);
-        put_i32(&dst->arg, s.arg);
-        publish();
-        s_last = count_up(&a.cnt1[row]) == (unsigned)NC - 1u;
-    }
-    __syncthreads();
-    if (!s_last || threadIdx.x >= 64) return;
-    combine_row<false>(a, b, i, row);
-    int last_row = 0;
-    if (threadIdx.x == 0) {
-        publish();
-        last_row = count_up(&a.seqcnt[b]) == (unsigned)K;
-    }
-    last_row = __shfl(last_row, 0);
-    if (last_row) resolve_greedy(a, b);
-}
-
-template <bool VEC>
-__device__ __forceinline__ void sample_item(const Args& a, int b, int i, int c)
-{
-    __shared__ int s_last, s_draw, s_owner, s_resid;
-    __shared__ double s_P, s_Q, s_T, s_lo;
+    __shared__ int s_last, s_n, s_owner;
+    __shared__ double s_base, s_T, s_P;
     const int NC = a.NC, K = a.K, V = a.V;
     const int64_t row = (int64_t)b * (K + 1) + i;
     const bool pair = i < K;
+    const float* prow = a.tp + row * V;
+    const float* qrow = pair ? a.dp + ((int64_t)b * K + i) * V : a.zero;
+    const int qV = pair ? V : kChunk;       // the zero operand is one chunk long
+    const int qc = pair ? c : 0;
 
     float4 pv[kVec], qv[kVec];
-    load_chunk<VEC>(a.tp + row * V, V, c, pv);
-    if (pair) {
-        load_chunk<VEC>(a.dp + ((int64_t)b * K + i) * V, V, c, qv);
-    } else {
-#pragma unroll
-        for (int k = 0; k < kVec; ++k) qv[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    const Acc t = pair ? thread_stats<true>(pv, qv, V, c) : thread_stats<false>(pv, qv, V, c);
-    reg_barrier(pv);
-    reg_barrier(qv);
-    const Acc s = pair ? block_reduce<true>(t) : block_reduce<false>(t);
+    load_chunk<VEC, true>(prow, V, c, pv);
+    load_chunk<VEC, true>(qrow, qV, qc, qv);
+    const Acc t = thread_stats<true>(pv, qv, V, c);
+    const Acc s = block_reduce<true>(t);
 
-    // rendezvous 1: row masses, argmax, acceptance
     if (threadIdx.x == 0) {
         ChunkPart* dst = &a.parts[row * NC + c];
         put_f64(&dst->sp, s.sp);
-        if (pair) {
-            put_f64(&dst->sq, s.sq);
-            put_f64(&dst->smin, s.smin);
-        }
+        put_f64(&dst->sq, s.sq);
+        put_f64(&dst->smin, s.smin);
         put_f32(&dst->maxv, s.maxv);
         put_i32(&dst->arg, s.arg);
         publish();
         s_last = count_up(&a.cnt1[row]) == (unsigned)NC - 1u;
     }
     __syncthreads();
-    if (s_last) {
-        if (threadIdx.x < 64) combine_row<true>(a, b, i, row);
-    } else if (threadIdx.x == 0) {
-        wait_flag(&a.flag1[row], a.hdr, a.wait_ticks);
+    if (!s_last) return;
+
+    // last block of the row: combine it, decide its draft's acceptance
+    if (threadIdx.x < 64) {
+        const RowView rv = combine_row<true>(a.parts + row * NC, NC);
+        int last_row = 0;
+        if (threadIdx.x == 0) {
+            const int tk = pair ? a.dt[(int64_t)b * K + i] : -1;
+            const bool tin = tk >= 0 && tk < V;
+            const float pt = tin ? prow[tk] : 0.0f;
+            const float qt = tin ? qrow[tk] : 0.0f;
+            int acc = 1;
+            if (pair) {
+                const double ui = (double)a.u[(int64_t)b * (K + 1) + i];
+                acc = (ui * (double)qt * rv.P < (double)pt * rv.Q) ? 1 : 0;
+            }
+            RowRes* rr = &a.rowres[row];
+            put_f64(&rr->P, rv.P);
+            put_f64(&rr->Q, rv.Q);
+            put_i32(&rr->acc, acc);
+            put_i32(&rr->arg, rv.arg);
+            if (a.stats) write_stats(a, row, rv, pair, pt, qt, pair);
+            publish();
+            last_row = count_up(&a.seqcnt[b]) == (unsigned)K;
+        }
+        last_row = __shfl(last_row, 0);
+        int n = -1;
+        if (last_row) {
+            // the sequence's last row: accept-prefix length, and the bonus
+            // chunk when every draft was accepted
+            observe();
+            n = first_rejection(a, b);
+            if (n == K) {
+                const int64_t rk = (int64_t)b * (K + 1) + K;
+                const double m = threadIdx.x < NC ? get_f64(&a.parts[rk * NC + threadIdx.x].sp) : 0.0;
+                int owner;
+                double base, T;
+                const double uK = (double)a.u[(int64_t)b * (K + 1) + K];
+                const double P = locate_chunk(m, NC, uK, &owner, &base, &T);
+                if (threadIdx.x == 0) {
+                    s_owner = owner;
+                    s_base = base;
+                    s_T = T;
+                    s_P = P;
+                }
+            }
+        }
+        if (threadIdx.x == 0) s_n = n;
     }
     __syncthreads();
+    const int n = s_n;
+    if (n < 0) return;                       // not the sequence's last row
+    if (n < K) {
+        // the residual tickets of this sequence take over
+        if (threadIdx.x == 0) {
+            put_i32(&a.seqinfo[b].n, n);
+            publish();
+            put_u32(&a.seqinfo[b].resolved, 1u);
+        }
+        return;
+    }
+    // every draft accepted: draw the bonus token from p_K
+    const int64_t rk = (int64_t)b * (K + 1) + K;
+    int x = -1;
+    if (s_owner >= 0) x = chunk_draw<VEC, false>(a.tp + rk * V, a.tp + rk * V, V, s_P, 0.0, s_owner, s_base, s_T);
     if (threadIdx.x == 0) {
-        const RowRes* rr = &a.rowres[row];
-        s_P = get_f64(&rr->P);
-        s_Q = get_f64(&rr->Q);
-        s_draw = get_i32(&rr->draw);
+        a.n_out[b] = K;
+        a.next_out[b] = x;
+        put_i32(&a.seqinfo[b].n, K);
+        publish();
+        put_u32(&a.seqinfo[b].resolved, 1u);
+    }
+}
+
+// Residual ticket: chunk c of the residual row of sequence b.
+template <bool VEC>
+__device__ __forceinline__ void resid_item(const Args& a, int b, int c)
+{
+    __shared__ int s_n, s_last, s_owner, s_resid;
+    __shared__ double s_P, s_Q, s_base, s_T;
+    const int NC = a.NC, K = a.K, V = a.V;
+    if (threadIdx.x == 0) {
+        wait_flag(&a.seqinfo[b].resolved, a.hdr, a.wait_ticks);
+        const int n = get_i32(&a.seqinfo[b].n);
+        s_n = n;
+        if (n < K) {
+            const RowRes* rr = &a.rowres[(int64_t)b * (K + 1) + n];
+            s_P = get_f64(&rr->P);
+            s_Q = get_f64(&rr->Q);
+        }
     }
     __syncthreads();
+    const int n = s_n;
+    if (n >= K) {                            // nothing to draw: count, and clean up last
+        if (threadIdx.x == 0) s_last = count_up(&a.cnt2[b]) == (unsigned)NC - 1u;
+        __syncthreads();
+        if (s_last && threadIdx.x < 64) {
+            observe();
+            zero_sequence(a, b);
+        }
+        return;
+    }
+    const int64_t row = (int64_t)b * (K + 1) + n;
+    const float* prow = a.tp + row * V;
+    const float* qrow = a.dp + ((int64_t)b * K + n) * V;
     const double P = s_P, Q = s_Q;
 
-    if (s_draw) {
+    // this chunk's residual mass (the rows were streamed moments ago, so
+    // these cached loads hit the Infinity Cache); a quarter chunk at a time
+    double w = 0.0;
+#pragma unroll 4
+    for (int k = 0; k < kVec; ++k) {
+        const float4 p4 = load_one<VEC>(prow, V, c, k), q4 = load_one<VEC>(qrow, V, c, k);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w += resid(comp(p4, e), comp(q4, e), P, Q);
+    }
+    w = block_sum(w);
+    if (threadIdx.x == 0) {
+        put_f64(&a.wpart[(int64_t)b * NC + c], w);
+        publish();
+        s_last = count_up(&a.cnt2[b]) == (unsigned)NC - 1u;
+    }
+    __syncthreads();
+    if (!s_last) return;
+
+    // last residual ticket: locate the chunk of u_K * W and draw there
+    if (threadIdx.x < 64) {
+        observe();
         const double uK = (double)a.u[(int64_t)b * (K + 1) + K];
-        if (pair) {
-            // rendezvous 2: residual masses of the rejecting row
-            double wsum = 0.0;
-#pragma unroll
-            for (int k = 0; k < kVec; ++k) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const double d = (double)comp(pv[k], e) * Q - (double)comp(qv[k], e) * P;
-                    wsum += d > 0.0 ? d : 0.0;
-                }
-            }
-            wsum = block_sum(wsum);
-            if (threadIdx.x == 0) {
-                put_f64(&a.wpart[row * NC + c], wsum);
-                publish();
-                s_last = count_up(&a.cnt2[row]) == (unsigned)NC - 1u;
-            }
-            __syncthreads();
-            if (s_last) {
-                if (threadIdx.x < 64) combine_residual(a, row);
-            } else if (threadIdx.x == 0) {
-                wait_flag(&a.flag2[row], a.hdr, a.wait_ticks);
-            }
-            __syncthreads();
+        const double m = threadIdx.x < NC ? get_f64(&a.wpart[(int64_t)b * NC + threadIdx.x]) : 0.0;
+        int owner;
+        double base, T;
+        const double W = locate_chunk(m, NC, uK, &owner, &base, &T);
+        int rs = 1;
+        if (!(W > 0.0)) {
+            // rounding left no residual mass: draw from p_n itself
+            const double mp = threadIdx.x < NC ? get_f64(&a.parts[row * NC + threadIdx.x].sp) : 0.0;
+            locate_chunk(mp, NC, uK, &owner, &base, &T);
+            rs = 0;
         }
         if (threadIdx.x == 0) {
-            const double* pref = a.prefp + row * (NC + 1);
-            double mass = P;
-            int resid = 0;
-            if (pair) {
-                const double W = get_f64(&a.prefw[row * (NC + 1) + NC]);
-                if (W > 0.0) {
-                    pref = a.prefw + row * (NC + 1);
-                    mass = W;
-                    resid = 1;
-                }
-            }
-            const double T = uK * mass;
-            const double lo = get_f64(&pref[c]), hi = get_f64(&pref[c + 1]);
-            s_owner = (lo <= T && T < hi) ? 1 : 0;
-            s_resid = resid;
+            s_owner = owner;
+            s_base = base;
             s_T = T;
-            s_lo = lo;
-        }
-        __syncthreads();
-        if (s_owner) {
-            const int x = s_resid ? chunk_draw<true>(pv, qv, P, Q, c, s_lo, s_T)
-                                  : chunk_draw<false>(pv, qv, P, Q, c, s_lo, s_T);
-            if (threadIdx.x == 0) put_i32(&a.rowres[row].cand, x);
+            s_resid = rs;
         }
     }
+    __syncthreads();
+    int x = -1;
+    if (s_owner >= 0)
+        x = s_resid ? chunk_draw<VEC, true>(prow, qrow, V, P, Q, s_owner, s_base, s_T)
+                    : chunk_draw<VEC, false>(prow, prow, V, P, Q, s_owner, s_base, s_T);
+    if (threadIdx.x < 64) {
+        if (threadIdx.x == 0) {
+            a.n_out[b] = n;
+            a.next_out[b] = x;
+        }
+        zero_sequence(a, b);
+    }
+}
 
-    // sequence completion
-    if (threadIdx.x == 0) {
-        const unsigned per_seq = (unsigned)(K + 1) * (unsigned)NC;
-        publish();
-        s_last = count_up(&a.seqcnt[b]) == per_seq - 1u;
+// Ticket order: sequences in order; row tickets of sequence r are followed
+// by the residual tickets of sequence r - lag.
+struct Ticket {
+    int kind;                // 0 row, 1 residual
+    int b, i, c;
+};
+
+__device__ __forceinline__ Ticket decode(const Args& a, unsigned tk)
+{
+    const unsigned NC = (unsigned)a.NC, P1 = (unsigned)(a.K + 1) * NC, RI = NC;
+    const unsigned D = (unsigned)a.lag, Bs = (unsigned)a.B;
+    const unsigned partA = D * P1, partB = (Bs - D) * (P1 + RI);
+    Ticket t{};
+    if (tk < partA) {
+        const unsigned r = tk / P1, off = tk - r * P1;
+        t = Ticket{0, (int)r, (int)(off / NC), (int)(off % NC)};
+    } else if (tk < partA + partB) {
+        const unsigned x = tk - partA, r = D + x / (P1 + RI), off = x % (P1 + RI);
+        if (off < P1)
+            t = Ticket{0, (int)r, (int)(off / NC), (int)(off % NC)};
+        else
+            t = Ticket{1, (int)(r - D), 0, (int)(off - P1)};
+    } else {
+        const unsigned x = tk - partA - partB;
+        t = Ticket{1, (int)(Bs - D + x / RI), 0, (int)(x % RI)};
     }
-    __syncthreads();
-    if (s_last && threadIdx.x < 64) resolve_sampled(a, b);
-    __syncthreads();
+    return t;
 }
 
 template <bool VEC>
-__global__ __launch_bounds__(kThreads, 2) void sv_sample_kernel(Args a)
+__global__ __launch_bounds__(kThreads, 4) void sv_sample_kernel(Args a)
 {
     __shared__ unsigned s_ticket;
-    const unsigned per_seq = (unsigned)(a.K + 1) * (unsigned)a.NC;
     for (;;) {
         if (threadIdx.x == 0) s_ticket = count_up(&a.hdr->ticket);   // carries no data
         __syncthreads();
-        const unsigned tk = s_ticket;
+        const unsigned tk = __builtin_amdgcn_readfirstlane(s_ticket);
         __syncthreads();
         if (tk >= a.total) break;
-        const int b = (int)(tk / per_seq);
-        const unsigned r = tk - (unsigned)b * per_seq;
-        const int i = (int)(r / (unsigned)a.NC);
-        const int c = (int)(r - (unsigned)i * (unsigned)a.NC);
-        sample_item<VEC>(a, b, i, c);
+        const Ticket t = decode(a, tk);
+        if (t.kind == 0)
+            row_item<VEC>(a, t.b, t.i, t.c);
+        else
+            resid_item<VEC>(a, t.b, t.c);
+        __syncthreads();
     }
     if (threadIdx.x == 0) {
         if (count_up(&a.hdr->exit_count) == gridDim.x - 1u) {
@@ -880,7 +987,7 @@ sv_status check_sizes(int32_t B, int32_t K, int32_t V)
     if (B < 0 || K < 0 || V < 1) return SV_ERR_INVALID_ARG;
     if (V > SV_MAX_V || K > SV_MAX_K) return SV_ERR_UNSUPPORTED;
     const uint64_t NC = ((uint64_t)V + kChunk - 1) / kChunk;
-    if ((uint64_t)B * (uint64_t)(K + 1) * NC >= (1ull << 31)) return SV_ERR_UNSUPPORTED;
+    if ((uint64_t)B * (uint64_t)(K + 2) * NC >= (1ull << 31)) return SV_ERR_UNSUPPORTED;
     return SV_OK;
 }
 
@@ -893,19 +1000,17 @@ Args make_args(void* ws, int32_t B, int32_t K, int32_t V)
     a.hdr = reinterpret_cast<Header*>(w + L.hdr);
     a.cnt1 = reinterpret_cast<unsigned*>(w + L.cnt1);
     a.cnt2 = reinterpret_cast<unsigned*>(w + L.cnt2);
-    a.flag1 = reinterpret_cast<unsigned*>(w + L.flag1);
-    a.flag2 = reinterpret_cast<unsigned*>(w + L.flag2);
     a.seqcnt = reinterpret_cast<unsigned*>(w + L.seqcnt);
+    a.seqinfo = reinterpret_cast<SeqInfo*>(w + L.seqinfo);
     a.rowres = reinterpret_cast<RowRes*>(w + L.rowres);
     a.parts = reinterpret_cast<ChunkPart*>(w + L.parts);
     a.wpart = reinterpret_cast<double*>(w + L.wpart);
-    a.prefp = reinterpret_cast<double*>(w + L.prefp);
-    a.prefw = reinterpret_cast<double*>(w + L.prefw);
+    a.zero = reinterpret_cast<const float*>(w + L.zero);
     a.B = B;
     a.K = K;
     a.V = V;
     a.NC = NC;
-    a.total = (unsigned)((uint64_t)B * (uint64_t)(K + 1) * (uint64_t)NC);
+    a.lag = B < kLag ? B : kLag;
     return a;
 }
 
@@ -955,6 +1060,7 @@ sv_status sv_verify_greedy_batched(const float* target_probs, const int32_t* dra
     a.n_out = n_accepted;
     a.next_out = next_token;
     a.stats = stats;
+    a.total = (unsigned)((uint64_t)B * (uint64_t)(K + 1) * (uint64_t)a.NC);
     const bool vec = (V % 4 == 0) && aligned(target_probs, 16);
     const dim3 grid(a.total), block(kThreads);
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -996,11 +1102,10 @@ sv_status sv_verify_sample_batched(const float* target_probs, const float* draft
     a.next_out = next_token;
     a.stats = stats;
     a.wait_ticks = (unsigned long long)(kWaitSeconds * 1000.0 * (double)d.wall_khz);
-    const bool vec = (V % 4 == 0) && aligned(target_probs, 16) && aligned(draft_probs, 16);
+    a.total = (unsigned)((uint64_t)B * (uint64_t)(K + 2) * (uint64_t)a.NC);   // row + residual tickets
+    const bool vec = (V % 4 == 0) && aligned(target_probs, 16) && (K == 0 || aligned(draft_probs, 16));
     const int occ = d.occ[vec ? 1 : 0];
-    const uint64_t resident = (uint64_t)occ * (uint64_t)d.cus;
-    // the row rendezvous needs every chunk of one row resident at once
-    if (resident < (uint64_t)a.NC) return SV_ERR_UNSUPPORTED;
+    const uint64_t resident = (uint64_t)(occ > 0 ? occ : 1) * (uint64_t)d.cus;
     const unsigned grid = (unsigned)(resident < a.total ? resident : a.total);
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (vec)
