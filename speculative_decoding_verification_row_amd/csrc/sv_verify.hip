@@ -56,6 +56,7 @@ constexpr int kChunk = kChunk4 * 4;            // 8192 values per chunk
 constexpr int kMaxChunks = 64;                 // one chunk per lane of a wave
 static_assert(SV_MAX_V == kMaxChunks * kChunk, "SV_MAX_V must match the chunk geometry");
 constexpr int kLag = 16;                       // residual tickets trail their sequence
+constexpr unsigned kTicketBatch = 4;           // tickets per atomic
 constexpr double kWaitSeconds = 2.0;           // bound of the one cross-block wait
 
 struct Header {              // 256 bytes
@@ -914,17 +915,23 @@ __global__ __launch_bounds__(kThreads, 4) void sv_sample_kernel(Args a)
 {
     __shared__ unsigned s_ticket;
     for (;;) {
-        if (threadIdx.x == 0) s_ticket = count_up(&a.hdr->ticket);   // carries no data
+        // one atomic hands out kTicketBatch consecutive tickets: the counter
+        // is the one hot address of the launch.  A block processes its batch
+        // in order; the progress argument holds because a block waits only on
+        // a sequence whose row tickets all precede its current ticket.
+        if (threadIdx.x == 0) s_ticket = kTicketBatch * count_up(&a.hdr->ticket);
         __syncthreads();
-        const unsigned tk = __builtin_amdgcn_readfirstlane(s_ticket);
+        const unsigned tk0 = __builtin_amdgcn_readfirstlane(s_ticket);
         __syncthreads();
-        if (tk >= a.total) break;
-        const Ticket t = decode(a, tk);
-        if (t.kind == 0)
-            row_item<VEC>(a, t.b, t.i, t.c);
-        else
-            resid_item<VEC>(a, t.b, t.c);
-        __syncthreads();
+        if (tk0 >= a.total) break;
+        for (unsigned tk = tk0; tk < tk0 + kTicketBatch && tk < a.total; ++tk) {
+            const Ticket t = decode(a, tk);
+            if (t.kind == 0)
+                row_item<VEC>(a, t.b, t.i, t.c);
+            else
+                resid_item<VEC>(a, t.b, t.c);
+            __syncthreads();
+        }
     }
     if (threadIdx.x == 0) {
         if (count_up(&a.hdr->exit_count) == gridDim.x - 1u) {
