@@ -98,6 +98,12 @@ def main():
     ap.add_argument("--mode", default=None, choices=[None, "sampled", "greedy"])
     ap.add_argument("--sets", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--gen-workers", type=int, default=None,
+                    help="processes generating the inputs (default: the usable CPUs, at most "
+                         "16; use 1 under a profiler)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy 5 times (reference for "
+                         "rocprofv3 FETCH_SIZE / WRITE_SIZE scaling)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -125,7 +131,8 @@ def main():
 
     sets = []
     for s in range(args.sets):
-        sets.append(device_batch(cfg["family"], B, K, V, seed=s, device=dev, sampled=sampled))
+        sets.append(device_batch(cfg["family"], B, K, V, seed=s, device=dev, sampled=sampled,
+                                 workers=args.gen_workers))
         log(f"  set {s} ready ({sets[-1]['sha256'][:12]})")
     n_out = torch.empty(B, dtype=torch.int32, device=dev)
     x_out = torch.empty(B, dtype=torch.int32, device=dev)
@@ -196,6 +203,16 @@ def main():
         "context": {"pages_cpu_latency_us": {"greedy": 33, "sampled": 117,
                                              "hardware": "Raspberry Pi 5, V=32000, K=4, one sequence"}},
     }
+    if args.copy_calibration:
+        # a plain copy kernel of known size: 1 GiB read + 1 GiB written per
+        # launch (an elementwise kernel; a device-to-device copy_ may run on a
+        # DMA engine that the counters do not see)
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        line["copy_calibration_bytes"] = src.numel() * 4
     if not args.no_cpu_baseline:
         log("timing the CPU oracle baseline")
         line["cpu_baseline"] = cpu_baseline(cfg, mode)

@@ -56,7 +56,7 @@ constexpr int kChunk = kChunk4 * 4;            // 8192 values per chunk
 constexpr int kMaxChunks = 64;                 // one chunk per lane of a wave
 static_assert(SV_MAX_V == kMaxChunks * kChunk, "SV_MAX_V must match the chunk geometry");
 constexpr int kLag = 16;                       // residual tickets trail their sequence
-constexpr unsigned kTicketBatch = 4;           // tickets per atomic
+constexpr unsigned kTicketBatch = 4;           // tickets per atomic on large launches
 constexpr double kWaitSeconds = 2.0;           // bound of the one cross-block wait
 
 struct Header {              // 256 bytes
@@ -124,6 +124,7 @@ struct Args {
     const float* zero;       // one chunk of zeros (the bonus row's draft operand)
     int B, K, V, NC;
     int lag;                 // min(kLag, B)
+    unsigned batch;          // tickets per atomic (sampled)
     unsigned total;          // work tickets (sampled)
     unsigned long long wait_ticks;   // wait bound in wall-clock ticks
 };
@@ -919,12 +920,12 @@ __global__ __launch_bounds__(kThreads, 4) void sv_sample_kernel(Args a)
         // is the one hot address of the launch.  A block processes its batch
         // in order; the progress argument holds because a block waits only on
         // a sequence whose row tickets all precede its current ticket.
-        if (threadIdx.x == 0) s_ticket = kTicketBatch * count_up(&a.hdr->ticket);
+        if (threadIdx.x == 0) s_ticket = a.batch * count_up(&a.hdr->ticket);
         __syncthreads();
         const unsigned tk0 = __builtin_amdgcn_readfirstlane(s_ticket);
         __syncthreads();
         if (tk0 >= a.total) break;
-        for (unsigned tk = tk0; tk < tk0 + kTicketBatch && tk < a.total; ++tk) {
+        for (unsigned tk = tk0; tk < tk0 + a.batch && tk < a.total; ++tk) {
             const Ticket t = decode(a, tk);
             if (t.kind == 0)
                 row_item<VEC>(a, t.b, t.i, t.c);
@@ -1113,7 +1114,11 @@ sv_status sv_verify_sample_batched(const float* target_probs, const float* draft
     const bool vec = (V % 4 == 0) && aligned(target_probs, 16) && (K == 0 || aligned(draft_probs, 16));
     const int occ = d.occ[vec ? 1 : 0];
     const uint64_t resident = (uint64_t)(occ > 0 ? occ : 1) * (uint64_t)d.cus;
-    const unsigned grid = (unsigned)(resident < a.total ? resident : a.total);
+    // batch tickets only when there are many per resident block: on small
+    // launches a batch would serialise work that could run side by side
+    a.batch = a.total >= 16u * resident ? kTicketBatch : (a.total >= 4u * resident ? 2u : 1u);
+    const uint64_t blocks = (a.total + a.batch - 1) / a.batch;
+    const unsigned grid = (unsigned)(resident < blocks ? resident : blocks);
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (vec)
         hipLaunchKernelGGL(sv_sample_kernel<true>, dim3(grid), dim3(kThreads), 0, s, a);
