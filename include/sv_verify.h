@@ -24,9 +24,11 @@
  * caller (row statistics included); the library allocates nothing and keeps
  * no pointer after returning.  Calls are asynchronous on `stream` (a
  * hipStream_t; NULL means the default stream): outputs are valid once the
- * stream has reached the call.  The library keeps no state between calls
- * apart from the per-device properties it caches; calls on different streams
- * must use different workspaces.
+ * stream has reached the call.  Between calls the library keeps only the
+ * per-device properties it caches and, per workspace address, a count of the
+ * calls made on it (each call tags the words it publishes in the workspace
+ * with a number derived from that count); calls that share a workspace must
+ * not overlap, so calls on different streams must use different workspaces.
  *
  * Layouts (row-major, V contiguous, f32 = IEEE binary32):
  *   target_probs [B, K+1, V] f32    draft_probs [B, K, V] f32
@@ -82,10 +84,11 @@ typedef struct {
  * sv_verify_sample_batched).  Returns 0 for sizes the library rejects. */
 size_t sv_workspace_size(int32_t B, int32_t K, int32_t V, int32_t sampled);
 
-/* Zero a workspace on `stream` (a fill kernel; no memset node).  A
- * workspace must be initialised once before its first use and again after
- * any call that returned an error or reported a device fault through
- * sv_workspace_error.  Every successful verify call leaves it initialised.
+/* Zero a workspace on `stream` (a fill kernel; no memset node) and restart
+ * its call count.  Memory must be initialised this way before its first use
+ * as a workspace (the first call on an address the library has not seen also
+ * clears it).  Afterwards calls need no further initialisation: every 255th
+ * call on a workspace clears it again on its stream before it runs.
  * Errors: SV_ERR_WORKSPACE for NULL or non-16-byte-aligned memory,
  * SV_ERR_HIP when the launch fails. */
 sv_status sv_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
@@ -118,9 +121,11 @@ sv_status sv_verify_sample_batched(const float* target_probs, const float* draft
                                    sv_row_stats* stats, void* stream);
 
 /* Synchronously read the workspace's device-fault word into *error_out
- * (host memory): 0 when every call since the last sv_workspace_init
- * completed normally, non-zero if a cross-workgroup wait exceeded its bound
- * (the outputs of that call are then unspecified).  Waits for `stream`. */
+ * (host memory), waiting for `stream` first: 0 when every call since the
+ * last sv_workspace_init completed normally.  The current kernels never set
+ * it: a workgroup that waits longer than its bound for another workgroup's
+ * partial result computes that result itself (bit-identically), so waits
+ * cannot fail. */
 sv_status sv_workspace_error(const void* workspace, int32_t* error_out, void* stream);
 
 /* Static, human-readable name of a status code. */

@@ -136,6 +136,8 @@ def workspace_for(B: int, K: int, V: int, sampled: bool, device, stream=None) ->
     """An initialised workspace for (device, stream), grown on demand.  One
     workspace per stream: calls on different streams must not share one."""
     device = torch.device(device)
+    if device.index is None:
+        device = torch.device(device.type, torch.cuda.current_device())
     s = stream if stream is not None else torch.cuda.current_stream(device)
     key = (device.index, int(s.cuda_stream))
     need = max(sv_workspace_size(B, K, V, sampled), 256)

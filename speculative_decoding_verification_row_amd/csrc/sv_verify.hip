@@ -7,40 +7,50 @@
 // silent are stated in include/sv_verify.h.
 //
 // Work decomposition (the vocabulary axis is the long one):
-//   * every row of V values is cut into NC = ceil(V / 8192) chunks; a
-//     256-thread block (4 waves) streams one chunk of one row (and, in
-//     sampled mode, the same chunk of the matching draft row): each thread
-//     issues 8 coalesced, non-temporal 16-byte loads per operand;
-//   * per-chunk partials (fp64 masses, lowest-index argmax) are combined in
-//     lane (= chunk) order by the last block of the row to arrive, so every
-//     result depends on V alone, never on B, K, the launch shape or timing;
-//   * the last row of a sequence to complete resolves the accept-prefix
-//     length n (the first rejected draft, or K);
-//   * greedy: next token = argmax of row n; no block ever waits.
-//   * sampled: a persistent grid takes work tickets in order.  Row tickets
-//     (pass 1) never wait.  For each sequence b, NC residual tickets follow
-//     kLag sequences later in the ticket order; by then b is normally
-//     resolved and its rows were streamed moments ago, so the residual
-//     re-read of the rejected pair (p_n, q_n) is served by the Infinity Cache
-//     rather than HBM.  Each residual ticket adds its chunk's mass of
-//     w = max(0, p_n*Q - q_n*P); the last one combines them and the block
-//     whose chunk holds u_K * W runs the inverse-CDF search over that chunk.
-//     When every draft is accepted, the resolver draws the bonus token from
-//     p_K the same way (chunk masses of p_K locate the chunk), and the
-//     sequence's residual tickets do nothing but count.
+//   * every row of V values is cut into NC chunks (4096 values in sampled
+//     mode, 8192 in greedy mode).  One 256-thread block (4 waves) owns chunk
+//     column c of sequence b and walks the rows of b in order: target row 0
+//     with draft row 0, row 1, ..., and last the bonus row K (target only).
+//     Each thread issues coalesced, non-temporal 16-byte loads, and the next
+//     row's chunk is loaded while the current one is reduced, so a block
+//     keeps loads in flight.  The grid is B * NC blocks, one per (b, c).
+//   * per-chunk partials (fp64 masses of p, q and min(p, q); lowest-index
+//     argmax) are published to the workspace as tagged words (below).
+//   * sampled mode: once row i+1 is loading, the block gathers the partials
+//     of row i from the NC sibling blocks of sequence b (they walk the same
+//     rows at the same time), forms the row masses P_i and Q_i, and publishes
+//     its chunk's residual mass sum max(0, p*Q - q*P) from the row-i data it
+//     still holds in registers.  No row is read twice: the final draw
+//     re-reads a single chunk.
+//   * the block of chunk column 0 finishes the sequence after its walk: it
+//     combines the rows (in chunk order), takes the acceptance decisions and
+//     the accept-prefix length n, and emits the next token -- argmax of row n
+//     (greedy), or an inverse-CDF draw over the residual of row n or over
+//     the bonus row (sampled), whose chunk is located from the published
+//     chunk masses and then searched.
+//   * every result depends on V alone (fixed chunking and combine order),
+//     never on B, K, the launch shape or timing.
 //
-// Progress: the only wait is a residual ticket whose sequence is not yet
-// resolved.  All of that sequence's row tickets come earlier in the ticket
-// order, so they are held by running blocks, and row tickets never wait:
-// the sequence resolves.  The wait is also bounded in time (expiry raises
-// the workspace fault word instead of spinning forever).
+// Cross-block data and progress.  There are no counters and no
+// read-modify-write atomics in global memory.  Every published 8-byte word
+// carries the call's epoch (1..255, chosen by the host per workspace) in
+// bits that readers strip: the low 8 mantissa bits of an fp64 partial (a
+// relative change below 2^-44, the same for every reader) or the top byte of
+// an (argmax, max) word.  A reader polls until each word it needs carries
+// the current epoch.  If a word has not arrived within a time bound (its
+// producer has not been scheduled), the reader computes that partial itself
+// with the producer's arithmetic in the producer's order, so the value is
+// bit-identical.  No wait is unbounded, and correctness never depends on the
+// order in which workgroups are dispatched.
 
 #include <hip/hip_runtime.h>
 
 #include <climits>
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 #include <mutex>
+#include <unordered_map>
 
 #include "sv_verify.h"
 
@@ -50,59 +60,42 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kVec = 8;                        // float4 per thread per operand
-constexpr int kChunk4 = kThreads * kVec;       // float4 per chunk
-constexpr int kChunk = kChunk4 * 4;            // 8192 values per chunk
-constexpr int kMaxChunks = 64;                 // one chunk per lane of a wave
-static_assert(SV_MAX_V == kMaxChunks * kChunk, "SV_MAX_V must match the chunk geometry");
-constexpr int kLag = 16;                       // residual tickets trail their sequence
-constexpr unsigned kTicketBatch = 4;           // tickets per atomic on large launches
-constexpr double kWaitSeconds = 2.0;           // bound of the one cross-block wait
+constexpr int kVecS = 4;                        // float4 per thread per operand (sampled)
+constexpr int kVecG = 8;                        // float4 per thread (greedy)
+constexpr int kChunkS = kThreads * kVecS * 4;   // 4096 values
+constexpr int kChunkG = kThreads * kVecG * 4;   // 8192 values
+constexpr int kMaxNC = 128;                     // two chunks per lane of a wave
+constexpr int kGroup = kWaves;                  // rows the finisher combines at a time
+static_assert(SV_MAX_V == kMaxNC * kChunkS, "SV_MAX_V must match the chunk geometry");
+constexpr unsigned kEpochs = 255;               // tags 1..255; 0 marks a cleared word
+constexpr double kPollMicroseconds = 200.0;     // bound of a wait before recomputing
 
 struct Header {              // 256 bytes
-    unsigned ticket;         // next work ticket (sampled)
-    unsigned exit_count;     // blocks that left the ticket loop (sampled)
-    unsigned error;          // sticky fault word: a bounded wait expired
-    unsigned pad[61];
+    unsigned error;          // fault word (reserved: nothing in this version sets it)
+    unsigned slow_path;      // 1 once a reader has recomputed a partial
+    unsigned pad[62];
 };
 
-struct ChunkPart {           // 32 bytes
-    double sp, sq, smin;     // chunk sums of p, q, min(p, q)
-    float maxv;
-    int arg;
-};
-
-struct RowRes {              // 32 bytes
-    double P, Q;             // row masses
-    int acc, arg;            // acceptance bit of the row's draft, lowest-index argmax
-    int pad[2];
-};
-
-struct SeqInfo {             // 8 bytes
-    int n;                   // accept-prefix length
-    unsigned resolved;       // 1 once n is published
+struct Part {                // 32 bytes, one per (row, chunk); tagged words
+    unsigned long long sp, sq, smin;   // fp64 chunk sums of p, q, min(p, q)
+    unsigned long long am;             // max value (low 32 bits), argmax (bits 32..55)
 };
 
 struct Layout {
-    size_t hdr, cnt1, cnt2, seqcnt, seqinfo, rowres, parts, wpart, zero, total;
+    size_t hdr, parts, wpart, total;
 };
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-inline Layout make_layout(int64_t B, int64_t K, int64_t NC)
+inline int chunk_of(bool sampled) { return sampled ? kChunkS : kChunkG; }
+
+inline Layout make_layout(int64_t B, int64_t K, int64_t NC, bool sampled)
 {
-    const size_t R = (size_t)(B * (K + 1));
     Layout L{};
     size_t o = 0;
-    L.hdr = o;     o = align_up(o + sizeof(Header), 256);
-    L.cnt1 = o;    o = align_up(o + R * 4, 256);
-    L.cnt2 = o;    o = align_up(o + (size_t)B * 4, 256);
-    L.seqcnt = o;  o = align_up(o + (size_t)B * 4, 256);
-    L.seqinfo = o; o = align_up(o + (size_t)B * sizeof(SeqInfo), 256);
-    L.rowres = o;  o = align_up(o + R * sizeof(RowRes), 256);
-    L.parts = o;   o = align_up(o + R * (size_t)NC * sizeof(ChunkPart), 256);
-    L.wpart = o;   o = align_up(o + (size_t)B * (size_t)NC * 8, 256);
-    L.zero = o;    o = align_up(o + (size_t)kChunk * 4, 256);   // never written
+    L.hdr = o;   o = align_up(o + sizeof(Header), 256);
+    L.parts = o; o = align_up(o + (size_t)(B * (K + 1) * NC) * sizeof(Part), 256);
+    L.wpart = o; o = align_up(o + (sampled ? (size_t)(B * K * NC) * 8 : 0), 256);
     L.total = o;
     return L;
 }
@@ -116,47 +109,21 @@ struct Args {
     int32_t* next_out;
     sv_row_stats* stats;
     Header* hdr;
-    unsigned *cnt1, *cnt2, *seqcnt;
-    SeqInfo* seqinfo;
-    RowRes* rowres;
-    ChunkPart* parts;
-    double* wpart;
-    const float* zero;       // one chunk of zeros (the bonus row's draft operand)
+    Part* parts;
+    unsigned long long* wpart;       // residual chunk masses (sampled)
     int B, K, V, NC;
-    int lag;                 // min(kLag, B)
-    unsigned batch;          // tickets per atomic (sampled)
-    unsigned total;          // work tickets (sampled)
-    unsigned long long wait_ticks;   // wait bound in wall-clock ticks
+    unsigned epoch;                  // this call's tag, 1..255
+    int force_recompute;             // test hook: readers recompute every partial
+    unsigned long long poll_ticks;   // wait bound in wall-clock ticks
 };
 
 // ------------------------------------------- cross-block communication --
-//
-// Every value one block publishes for another (chunk partials, row results,
-// counters) is written and read with agent-scope atomic accesses.  On gfx950
-// these are performed at the device-coherent level (sc1 loads and stores;
-// RMW atomics at the memory side) instead of in the per-XCD L2, so no L2
-// write-back or invalidate (the cost of agent-scope release/acquire fences)
-// is ever needed.  Ordering is explicit:
-//   writer: data stores -> publish() -> counter RMW or flag store
-//   reader: counter RMW or flag load -> observe() -> data loads
-// publish() waits for the wave's outstanding memory operations to complete
-// (gfx9 counts stores in vmcnt); both are compiler barriers.
 
-__device__ __forceinline__ void publish() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-__device__ __forceinline__ void observe() { asm volatile("" ::: "memory"); }
+// Published words are written and read with agent-scope atomic accesses,
+// which gfx950 performs at the device-coherent level (no per-XCD L2 copy is
+// involved, so no cache write-back or invalidate is needed).  Each word
+// validates itself through its tag, so no ordering between words is needed.
 
-__device__ __forceinline__ unsigned count_up(unsigned* p)
-{
-    return __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void put_u32(void* p, unsigned v)
-{
-    __hip_atomic_store(static_cast<unsigned*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ unsigned get_u32(const void* p)
-{
-    return __hip_atomic_load(static_cast<const unsigned*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 __device__ __forceinline__ void put_u64(void* p, unsigned long long v)
 {
     __hip_atomic_store(static_cast<unsigned long long*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -166,124 +133,104 @@ __device__ __forceinline__ unsigned long long get_u64(const void* p)
     return __hip_atomic_load(static_cast<const unsigned long long*>(p), __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void put_i32(int* p, int v) { put_u32(p, (unsigned)v); }
-__device__ __forceinline__ int get_i32(const int* p) { return (int)get_u32(p); }
-__device__ __forceinline__ void put_f32(float* p, float v) { put_u32(p, __float_as_uint(v)); }
-__device__ __forceinline__ float get_f32(const float* p) { return __uint_as_float(get_u32(p)); }
-__device__ __forceinline__ void put_f64(double* p, double v)
+__device__ __forceinline__ void put_u32(void* p, unsigned v)
 {
-    put_u64(p, (unsigned long long)__double_as_longlong(v));
-}
-__device__ __forceinline__ double get_f64(const double* p)
-{
-    return __longlong_as_double((long long)get_u64(p));
+    __hip_atomic_store(static_cast<unsigned*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Bounded wait until *flag != 0; on expiry raises the fault word and returns
-// (the call's outputs are then unspecified, but every block exits).
-__device__ __forceinline__ void wait_flag(const unsigned* flag, Header* hdr, unsigned long long ticks)
+__device__ __forceinline__ unsigned long long tag_f64(double v, unsigned ep)
 {
-    const unsigned long long t0 = wall_clock64();
-    while (get_u32(flag) == 0u) {
-        __builtin_amdgcn_s_sleep(8);
-        if (wall_clock64() - t0 > ticks) {
-            put_u32(&hdr->error, 1u);
-            break;
-        }
-    }
-    observe();
+    return ((unsigned long long)__double_as_longlong(v) & ~0xFFull) | ep;
 }
-
-// Wave-cooperative zeroing of [p, p + bytes), p 8-byte aligned, bytes % 8 == 0.
-__device__ __forceinline__ void wave_zero(void* p, size_t bytes)
+__device__ __forceinline__ bool f64_ok(unsigned long long w, unsigned ep) { return (w & 0xFFull) == ep; }
+__device__ __forceinline__ double f64_of(unsigned long long w)
 {
-    unsigned long long* q = static_cast<unsigned long long*>(p);
-    const size_t n = bytes / 8;
-    for (size_t j = threadIdx.x & 63; j < n; j += 64) put_u64(q + j, 0ull);
+    return __longlong_as_double((long long)(w & ~0xFFull));
 }
+// the value every reader obtains for a published fp64 partial
+__device__ __forceinline__ double strip8(double v) { return f64_of((unsigned long long)__double_as_longlong(v)); }
 
-// Once sequence b is finished nothing reads its counters, partials or row
-// results again: return them to zero so that the whole workspace is zero
-// between calls, whatever shapes the next call uses.  One wave calls it.
-__device__ __forceinline__ void zero_sequence(const Args& a, int b)
+__device__ __forceinline__ unsigned long long tag_am(float v, int arg, unsigned ep)
 {
-    const int64_t rows = a.K + 1, r0 = (int64_t)b * rows, NC = a.NC;
-    wave_zero(a.parts + r0 * NC, (size_t)(rows * NC) * sizeof(ChunkPart));
-    wave_zero(a.rowres + r0, (size_t)rows * sizeof(RowRes));
-    wave_zero(a.wpart + (int64_t)b * NC, (size_t)NC * 8);
-    for (int64_t j = threadIdx.x & 63; j < rows; j += 64) put_u32(&a.cnt1[r0 + j], 0u);
-    if ((threadIdx.x & 63) == 0) {
-        put_u32(&a.cnt2[b], 0u);
-        put_u32(&a.seqcnt[b], 0u);
-        put_u64(&a.seqinfo[b], 0ull);
-    }
+    return ((unsigned long long)((ep << 24) | (unsigned)arg) << 32) | (unsigned long long)__float_as_uint(v);
+}
+__device__ __forceinline__ bool am_ok(unsigned long long w, unsigned ep) { return (unsigned)(w >> 56) == ep; }
+__device__ __forceinline__ float am_val(unsigned long long w) { return __uint_as_float((unsigned)w); }
+__device__ __forceinline__ int am_arg(unsigned long long w) { return (int)((w >> 32) & 0xFFFFFFu); }
+
+// Block-uniform bounded wait: true once the bound has passed (thread 0's
+// clock decides, so every thread leaves the wait loop together).
+__device__ __forceinline__ bool wait_expired(const Args& a, unsigned long long t0)
+{
+    return __syncthreads_or(threadIdx.x == 0 && (a.force_recompute || wall_clock64() - t0 > a.poll_ticks));
 }
 
 // ---------------------------------------------------------- chunk I/O --
 
-// Thread t holds float4 number (c * kChunk4 + k * 256 + t) of the row, k < 8:
-// consecutive threads read consecutive 16-byte words (fully coalesced).
-__device__ __forceinline__ int f4_index(int c, int k) { return c * kChunk4 + k * kThreads + (int)threadIdx.x; }
-
+// Rows are read through buffer resources: the row's base address lives in
+// scalar registers and each thread keeps one 32-bit byte offset, and the
+// resource's range check returns 0 for every value at index V or beyond
+// without touching memory.  Those zeros cannot change a sum, and they cannot
+// become the argmax (values are non-negative and the lowest index wins a
+// tie), so no masking is needed anywhere.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+constexpr int kRsrcWord3 = 0x00020000;   // gfx9 raw buffer: 32-bit data format
+constexpr int kNonTemporal = 2;          // cache policy bit: streamed, not kept
 
-// Streaming load: every value is read once, so it is not kept in cache.
-__device__ __forceinline__ float4 load_stream(const float4* p)
+struct Row {
+    __amdgpu_buffer_rsrc_t r;
+};
+
+__device__ __forceinline__ Row row_of(const float* base, int V)
 {
-    const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
-    return make_float4(t.x, t.y, t.z, t.w);
+    return Row{__builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, V * 4, kRsrcWord3)};
 }
-__device__ __forceinline__ float load_stream(const float* p) { return __builtin_nontemporal_load(p); }
 
-// Loads of float4 numbers k in [0, kVec) of chunk c.  Every load is
-// unconditional (an out-of-range index is clamped to the row's last element)
-// and nothing is written to the destination registers afterwards: values
-// past the row's end are masked where they are consumed (thread_stats), so
-// all loads of a thread are in flight together.  STREAM selects the
-// non-temporal hint (first pass) or ordinary cached loads.
-template <bool VEC, bool STREAM>
-__device__ __forceinline__ void load_chunk(const float* __restrict__ row, int V, int c, float4 (&v)[kVec])
+// Thread t holds float4 number (c * 256 * NV + k * 256 + t) of the row,
+// k < NV: consecutive threads read consecutive 16-byte words (coalesced).
+template <int NV>
+__device__ __forceinline__ int f4_index(int c, int k) { return c * (kThreads * NV) + k * kThreads + (int)threadIdx.x; }
+
+__device__ __forceinline__ float4 as_float4(u32x4 v)
 {
-    if constexpr (VEC) {
-        const float4* r4 = reinterpret_cast<const float4*>(row);
-        const int nf = V >> 2;
+    return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
+}
+
+// Streaming loads of float4 numbers k in [0, NV) of chunk c; all of a
+// thread's loads are issued back to back and stay in flight together.  The
+// scalar form (rows not 16-byte aligned, or V not a multiple of 4) reads
+// the same values one float at a time.
+template <bool VEC, int NV>
+__device__ __forceinline__ void load_chunk(Row row, int c, float4 (&v)[NV])
+{
 #pragma unroll
-        for (int k = 0; k < kVec; ++k) {
-            const int f = f4_index(c, k);
-            const float4* src = r4 + (f < nf ? f : nf - 1);
-            v[k] = STREAM ? load_stream(src) : *src;
-        }
-    } else {
-#pragma unroll
-        for (int k = 0; k < kVec; ++k) {
-            const int x = f4_index(c, k) * 4;
+    for (int k = 0; k < NV; ++k) {
+        const int off = f4_index<NV>(c, k) * 16;
+        if constexpr (VEC) {
+            v[k] = as_float4(__builtin_amdgcn_raw_buffer_load_b128(row.r, off, 0, kNonTemporal));
+        } else {
             float e[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float* src = row + (x + j < V ? x + j : V - 1);
-                e[j] = STREAM ? load_stream(src) : *src;
-            }
+            for (int j = 0; j < 4; ++j)
+                e[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(row.r, off + 4 * j, 0, kNonTemporal));
             v[k] = make_float4(e[0], e[1], e[2], e[3]);
         }
     }
 }
 
-// Cached load of float4 number k (runtime) of chunk c, zero outside the row.
-template <bool VEC>
-__device__ __forceinline__ float4 load_one(const float* __restrict__ row, int V, int c, int k)
+// Cached load of float4 number k (runtime) of chunk c.
+template <bool VEC, int NV>
+__device__ __forceinline__ float4 load_one(Row row, int c, int k)
 {
+    const int off = f4_index<NV>(c, k) * 16;
     if constexpr (VEC) {
-        const float4* r4 = reinterpret_cast<const float4*>(row);
-        const int nf = V >> 2, f = f4_index(c, k);
-        const float4 v = r4[f < nf ? f : nf - 1];
-        return f < nf ? v : make_float4(0.f, 0.f, 0.f, 0.f);
+        return as_float4(__builtin_amdgcn_raw_buffer_load_b128(row.r, off, 0, 0));
     } else {
-        const int x = f4_index(c, k) * 4;
         float e[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) e[j] = row[x + j < V ? x + j : V - 1];
-        return make_float4(x + 0 < V ? e[0] : 0.f, x + 1 < V ? e[1] : 0.f,
-                           x + 2 < V ? e[2] : 0.f, x + 3 < V ? e[3] : 0.f);
+        for (int j = 0; j < 4; ++j) e[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(row.r, off + 4 * j, 0, 0));
+        return make_float4(e[0], e[1], e[2], e[3]);
     }
 }
 
@@ -301,6 +248,12 @@ __device__ __forceinline__ double resid(float p, float q, double P, double Q)
 
 // ------------------------------------------------------- reductions --
 
+// Which statistics a pass accumulates and publishes for a chunk.  The masses
+// P and Q decide acceptance, the argmax decides greedy verification, and the
+// remaining fields exist only for the optional per-row statistics output, so
+// a call without statistics leaves them out of the streamed pass.
+enum : int { kSP = 1, kSQ = 2, kSMIN = 4, kAM = 8 };
+
 struct Acc {
     double sp, sq, smin;
     float maxv;
@@ -317,33 +270,83 @@ __device__ __forceinline__ void argmax_merge(float& v, int& i, float ov, int oi)
     }
 }
 
-// Per-thread partials of one chunk as load_chunk left it: values at index
-// V or beyond (clamped duplicates) are masked to 0 here.
-template <bool PAIR>
-__device__ __forceinline__ Acc thread_stats(const float4 (&pv)[kVec], const float4 (&qv)[kVec], int V, int c)
+// Adds float4 number k of the thread's chunk share.  This is the single
+// definition of the per-thread order: the streamed path and the recompute
+// path both call it, and each field's sum is independent of which other
+// fields are accumulated.  While a thread accumulates, arg holds the
+// position 4k + e of its maximum among its own values (positions increase
+// with the index, so the first maximum is the lowest index); thread_arg()
+// turns it into the row index.
+template <int M>
+__device__ __forceinline__ void acc_f4(Acc& a, float4 p4, float4 q4, int k)
 {
-    Acc a{0.0, 0.0, 0.0, -INFINITY, INT_MAX};
 #pragma unroll
-    for (int k = 0; k < kVec; ++k) {
-        const int x0 = f4_index(c, k) * 4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const bool in = x0 + e < V;
-            const float p = in ? comp(pv[k], e) : 0.0f;
-            if (in && p > a.maxv) {
+    for (int e = 0; e < 4; ++e) {
+        const float p = comp(p4, e);
+        if constexpr ((M & kAM) != 0) {
+            if (p > a.maxv) {
                 a.maxv = p;
-                a.arg = x0 + e;
-            }
-            a.sp += (double)p;
-            if constexpr (PAIR) {
-                const float q = in ? comp(qv[k], e) : 0.0f;
-                a.sq += (double)q;
-                a.smin += (double)fminf(p, q);
+                a.arg = 4 * k + e;
             }
         }
+        if constexpr ((M & kSP) != 0) a.sp += (double)p;
+        if constexpr ((M & (kSQ | kSMIN)) != 0) {
+            const float q = comp(q4, e);
+            if constexpr ((M & kSQ) != 0) a.sq += (double)q;
+            if constexpr ((M & kSMIN) != 0) a.smin += (double)fminf(p, q);
+        }
+    }
+}
+
+// Row index of the thread-local position 4k + e in chunk c.
+template <int NV>
+__device__ __forceinline__ void thread_arg(Acc& a, int c)
+{
+    a.arg = f4_index<NV>(c, a.arg >> 2) * 4 + (a.arg & 3);
+}
+
+template <int M, int NV>
+__device__ __forceinline__ Acc thread_stats(const float4 (&pv)[NV], const float4 (&qv)[NV], int c)
+{
+    Acc a{0.0, 0.0, 0.0, -INFINITY, 0};
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+        acc_f4<M>(a, pv[k], qv[k], k);
         __builtin_amdgcn_sched_barrier(0);   // keep fp64 temporaries to one float4 at a time
     }
+    thread_arg<NV>(a, c);
     return a;
+}
+
+// The same per-thread sums, re-reading the chunk one float4 at a time.
+template <bool VEC, int M, int NV>
+__device__ __forceinline__ Acc thread_stats_reload(Row prow, Row qrow, int c)
+{
+    constexpr bool kQ = (M & (kSQ | kSMIN)) != 0;
+    Acc a{0.0, 0.0, 0.0, -INFINITY, 0};
+    for (int k = 0; k < NV; ++k) {
+        const float4 p4 = load_one<VEC, NV>(prow, c, k);
+        const float4 q4 = kQ ? load_one<VEC, NV>(qrow, c, k) : p4;
+        acc_f4<M>(a, p4, q4, k);
+    }
+    thread_arg<NV>(a, c);
+    return a;
+}
+
+__device__ __forceinline__ double resid_f4(float4 p4, float4 q4, double P, double Q)
+{
+    double w = 0.0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w += resid(comp(p4, e), comp(q4, e), P, Q);
+    return w;
+}
+
+template <bool VEC, int NV>
+__device__ __forceinline__ double thread_resid_reload(Row prow, Row qrow, int c, double P, double Q)
+{
+    double w = 0.0;
+    for (int k = 0; k < NV; ++k) w += resid_f4(load_one<VEC, NV>(prow, c, k), load_one<VEC, NV>(qrow, c, k), P, Q);
+    return w;
 }
 
 __device__ __forceinline__ double wave_sum(double v)
@@ -364,8 +367,9 @@ __device__ __forceinline__ double wave_inclusive_scan(double v)
     return v;
 }
 
-// Block reduction; the result is valid in thread 0.
-template <bool PAIR>
+// Block reduction of the fields in M; the result is valid in thread 0.
+// Ends with a barrier, so the block may call it again at once.
+template <int M>
 __device__ __forceinline__ Acc block_reduce(Acc a)
 {
     __shared__ double s_sp[kWaves], s_sq[kWaves], s_sm[kWaves];
@@ -373,14 +377,14 @@ __device__ __forceinline__ Acc block_reduce(Acc a)
     __shared__ int s_i[kWaves];
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
-        a.sp += __shfl_xor(a.sp, off);
-        if constexpr (PAIR) {
-            a.sq += __shfl_xor(a.sq, off);
-            a.smin += __shfl_xor(a.smin, off);
+        if constexpr ((M & kSP) != 0) a.sp += __shfl_xor(a.sp, off);
+        if constexpr ((M & kSQ) != 0) a.sq += __shfl_xor(a.sq, off);
+        if constexpr ((M & kSMIN) != 0) a.smin += __shfl_xor(a.smin, off);
+        if constexpr ((M & kAM) != 0) {
+            const float ov = __shfl_xor(a.maxv, off);
+            const int oi = __shfl_xor(a.arg, off);
+            argmax_merge(a.maxv, a.arg, ov, oi);
         }
-        const float ov = __shfl_xor(a.maxv, off);
-        const int oi = __shfl_xor(a.arg, off);
-        argmax_merge(a.maxv, a.arg, ov, oi);
     }
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     if (lane == 0) {
@@ -401,9 +405,11 @@ __device__ __forceinline__ Acc block_reduce(Acc a)
             argmax_merge(r.maxv, r.arg, s_v[j], s_i[j]);
         }
     }
+    __syncthreads();
     return r;
 }
 
+// Block sum; the result is valid in thread 0.  Ends with a barrier.
 __device__ __forceinline__ double block_sum(double v)
 {
     __shared__ double s[kWaves];
@@ -415,89 +421,239 @@ __device__ __forceinline__ double block_sum(double v)
         r = s[0];
         for (int j = 1; j < kWaves; ++j) r += s[j];
     }
+    __syncthreads();
     return r;
 }
 
-// ------------------------------------------------------ row combine --
+// Wave-cooperative sum of chunk values s[0..NC) in a fixed order: lane l
+// adds chunks l and l + 64, then a butterfly.  Every reader of a row uses
+// this one order, so all of them obtain the same row masses.
+__device__ __forceinline__ double sum_chunks(const double* s, int NC)
+{
+    const int lane = threadIdx.x & 63;
+    const double v = (lane < NC ? s[lane] : 0.0) + (lane + 64 < NC ? s[lane + 64] : 0.0);
+    return wave_sum(v);
+}
 
+// The acceptance test of a draft token (fp64, scale-free): accept iff
+// u * q(t) * P < p(t) * Q.  Every place that decides uses this expression.
+__device__ __forceinline__ bool accepted(float u, float pt, float qt, double P, double Q)
+{
+    return (double)u * (double)qt * P < (double)pt * Q;
+}
+
+// Publish the fields in M of a chunk's reduced statistics (thread 0).
+template <int M>
+__device__ __forceinline__ void publish_part(const Args& a, int64_t row, int c, const Acc& s)
+{
+    if (threadIdx.x == 0) {
+        Part* dst = &a.parts[row * a.NC + c];
+        if constexpr ((M & kSP) != 0) put_u64(&dst->sp, tag_f64(s.sp, a.epoch));
+        if constexpr ((M & kSQ) != 0) put_u64(&dst->sq, tag_f64(s.sq, a.epoch));
+        if constexpr ((M & kSMIN) != 0) put_u64(&dst->smin, tag_f64(s.smin, a.epoch));
+        if constexpr ((M & kAM) != 0) put_u64(&dst->am, tag_am(s.maxv, s.arg, a.epoch));
+    }
+}
+
+// ------------------------------------------------------ gathering --
+
+// The gathered partials of up to kGroup rows of one sequence.
+struct Gathered {
+    double sp[kGroup][kMaxNC];
+    double sq[kGroup][kMaxNC];
+    double smin[kGroup][kMaxNC];
+    unsigned long long am[kGroup][kMaxNC];
+};
+
+// LDS of a block: while it walks its chunk column, the chunk of the row
+// whose decision is pending (target float4s, then draft float4s; each thread
+// touches only its own column, so no barrier guards it); when it finishes a
+// sequence, the gathered partials.
+union LdsArea {
+    f32x4 parked[2 * kVecS][kThreads];
+    Gathered g;
+};
+__shared__ LdsArea lds;
+
+template <int M>
+__device__ __forceinline__ bool part_ok(const Part* pp, unsigned ep, int r, int c, bool store)
+{
+    const unsigned long long wsp = (M & kSP) ? get_u64(&pp->sp) : 0ull;
+    const unsigned long long wsq = (M & kSQ) ? get_u64(&pp->sq) : 0ull;
+    const unsigned long long wsm = (M & kSMIN) ? get_u64(&pp->smin) : 0ull;
+    const unsigned long long wam = (M & kAM) ? get_u64(&pp->am) : 0ull;
+    const bool ok = (!(M & kSP) || f64_ok(wsp, ep)) && (!(M & kSQ) || f64_ok(wsq, ep)) &&
+                    (!(M & kSMIN) || f64_ok(wsm, ep)) && (!(M & kAM) || am_ok(wam, ep));
+    if (ok && store) {
+        lds.g.sp[r][c] = f64_of(wsp);
+        lds.g.sq[r][c] = f64_of(wsq);
+        lds.g.smin[r][c] = f64_of(wsm);
+        lds.g.am[r][c] = wam;
+    }
+    return ok;
+}
+
+template <bool VEC, int M, int NV>
+__device__ void recompute_part(const Args& a, Row prow, Row qrow, int r, int c)
+{
+    const Acc s = block_reduce<M>(thread_stats_reload<VEC, M, NV>(prow, qrow, c));
+    if (threadIdx.x == 0) {
+        lds.g.sp[r][c] = strip8(s.sp);
+        lds.g.sq[r][c] = strip8(s.sq);
+        lds.g.smin[r][c] = strip8(s.smin);
+        lds.g.am[r][c] = tag_am(s.maxv, s.arg, a.epoch);
+        put_u32(&a.hdr->slow_path, 1u);
+    }
+}
+
+// Block-cooperative: read the partials of rows row0 .. row0 + nrows - 1 of
+// sequence b (rows numbered within the sequence) into lds.g: fields MROW of
+// rows below K and MLAST of row K.  Partials that do not carry this call's
+// tag within the wait bound are recomputed from the inputs.
+template <bool VEC, int NV, int MROW, int MLAST>
+__device__ void gather_rows(const Args& a, int b, int row0, int nrows)
+{
+    __shared__ unsigned long long s_miss[kGroup][2];
+    const int NC = a.NC, K = a.K, V = a.V;
+    const unsigned ep = a.epoch;
+    const int n_ent = nrows * NC;
+    constexpr int kPer = (kGroup * kMaxNC + kThreads - 1) / kThreads;   // entries per thread
+    bool need[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) need[j] = (int)threadIdx.x + j * kThreads < n_ent;
+    const unsigned long long t0 = wall_clock64();
+    for (;;) {
+        bool any = false;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            if (!need[j]) continue;
+            const int e = (int)threadIdx.x + j * kThreads, r = e / NC, c = e - r * NC;
+            const int i = row0 + r;
+            const Part* pp = &a.parts[((int64_t)b * (K + 1) + i) * NC + c];
+            const bool ok = i < K ? part_ok<MROW>(pp, ep, r, c, !a.force_recompute)
+                                  : part_ok<MLAST>(pp, ep, r, c, !a.force_recompute);
+            if (ok && !a.force_recompute)
+                need[j] = false;
+            else
+                any = true;
+        }
+        if (!__syncthreads_or(any)) break;
+        if (wait_expired(a, t0)) break;
+        __builtin_amdgcn_s_sleep(2);
+    }
+    // what is still missing (rare): recompute it, one chunk at a time
+    if (threadIdx.x < kGroup * 2) s_miss[threadIdx.x >> 1][threadIdx.x & 1] = 0ull;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        if (!need[j]) continue;
+        const int e = (int)threadIdx.x + j * kThreads, r = e / NC, c = e - r * NC;
+        atomicOr(&s_miss[r][c >> 6], 1ull << (c & 63));   // LDS
+    }
+    __syncthreads();
+    for (int r = 0; r < nrows; ++r) {
+        const int i = row0 + r;
+        const int64_t row = (int64_t)b * (K + 1) + i;
+        const Row prow = row_of(a.tp + row * V, V);
+        const bool has_q = i < K && (MROW & (kSQ | kSMIN)) != 0;
+        const Row qrow = has_q ? row_of(a.dp + ((int64_t)b * K + i) * V, V) : prow;
+        for (int h = 0; h < 2; ++h) {
+            unsigned long long mk = s_miss[r][h];
+            while (mk) {
+                const int c = h * 64 + __ffsll((unsigned long long)mk) - 1;
+                mk &= mk - 1;
+                if (i < K)
+                    recompute_part<VEC, MROW, NV>(a, prow, qrow, r, c);
+                else
+                    recompute_part<VEC, MLAST, NV>(a, prow, qrow, r, c);
+            }
+        }
+    }
+    __syncthreads();
+}
+
+// Wave-cooperative combine of gathered row r (values valid in every lane).
 struct RowView {
-    double P, Q, Smin;       // row masses
+    double P, Q, Smin;
     float maxv;
     int arg;
 };
 
-// Wave-cooperative (all 64 lanes of one wave): combine the NC chunk partials
-// of a row in lane (= chunk) order.
-template <bool PAIR>
-__device__ __forceinline__ RowView combine_row(const ChunkPart* parts, int NC)
+template <int M>
+__device__ __forceinline__ RowView combine_row(int r, int NC)
 {
     const int lane = threadIdx.x & 63;
-    observe();
-    double sp = 0.0, sq = 0.0, sm = 0.0;
-    float mv = -INFINITY;
-    int ai = INT_MAX;
-    if (lane < NC) {
-        sp = get_f64(&parts[lane].sp);
-        if constexpr (PAIR) {
-            sq = get_f64(&parts[lane].sq);
-            sm = get_f64(&parts[lane].smin);
+    RowView v{0.0, 0.0, 0.0, -INFINITY, INT_MAX};
+    if constexpr ((M & kSP) != 0) v.P = sum_chunks(lds.g.sp[r], NC);
+    if constexpr ((M & kSQ) != 0) v.Q = sum_chunks(lds.g.sq[r], NC);
+    if constexpr ((M & kSMIN) != 0) v.Smin = sum_chunks(lds.g.smin[r], NC);
+    if constexpr ((M & kAM) != 0) {
+        float mv = -INFINITY;
+        int ai = INT_MAX;
+        for (int h = 0; h < 2; ++h) {
+            const int c = lane + 64 * h;
+            if (c < NC) argmax_merge(mv, ai, am_val(lds.g.am[r][c]), am_arg(lds.g.am[r][c]));
         }
-        mv = get_f32(&parts[lane].maxv);
-        ai = get_i32(&parts[lane].arg);
-    }
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-        const float ov = __shfl_xor(mv, off);
-        const int oi = __shfl_xor(ai, off);
-        argmax_merge(mv, ai, ov, oi);
+        for (int off = 32; off > 0; off >>= 1) {
+            const float ov = __shfl_xor(mv, off);
+            const int oi = __shfl_xor(ai, off);
+            argmax_merge(mv, ai, ov, oi);
+        }
+        v.maxv = mv;
+        v.arg = ai;
     }
-    const double incl = wave_inclusive_scan(sp);
-    RowView r;
-    r.P = __shfl(incl, NC - 1);
-    r.Q = PAIR ? wave_sum(sq) : 0.0;
-    r.Smin = PAIR ? wave_sum(sm) : 0.0;
-    r.maxv = mv;
-    r.arg = ai;
-    return r;
-}
-
-// Wave-cooperative: given the NC chunk masses m[c] (lane c), the chunk that
-// holds T = u * (total) -- the one with prefix(c-1) <= T < prefix(c) -- and
-// its base prefix(c-1).  Prefixes are the inclusive scan in lane order; the
-// total is its last entry, so T < total always has an owner when total > 0.
-// Returns the total; *owner = -1 when no chunk qualifies (total == 0).
-__device__ __forceinline__ double locate_chunk(double m, int NC, double u, int* owner, double* base,
-                                               double* T_out)
-{
-    const int lane = threadIdx.x & 63;
-    const double incl = wave_inclusive_scan(lane < NC ? m : 0.0);
-    const double total = __shfl(incl, NC - 1);
-    const double T = u * total;
-    double lo = __shfl_up(incl, 1);
-    if (lane == 0) lo = 0.0;
-    const bool own = lane < NC && lo <= T && T < incl;
-    const unsigned long long mk = __ballot(own);
-    const int c = mk ? __ffsll((unsigned long long)mk) - 1 : -1;
-    *owner = c;
-    *base = c >= 0 ? __shfl(lo, c) : 0.0;
-    *T_out = T;
-    return total;
+    return v;
 }
 
 // ---------------------------------------------------- inverse CDF --
+
+// Wave-cooperative: given chunk masses m[0..NC) (chunks 2l and 2l+1 in lane
+// l), the chunk c with prefix(c-1) <= T < prefix(c) for T = u * total, and
+// its base prefix(c-1).  Prefixes are an inclusive scan in chunk order and
+// the total is its last entry, so T < total always has an owner when
+// total > 0.  Returns the total; *owner = -1 when total == 0.
+__device__ __forceinline__ double locate_chunk(const double* m, int NC, double u, int* owner, double* base,
+                                               double* T_out)
+{
+    const int lane = threadIdx.x & 63;
+    const int c0 = 2 * lane, c1 = 2 * lane + 1;
+    const double m0 = c0 < NC ? m[c0] : 0.0, m1 = c1 < NC ? m[c1] : 0.0;
+    const double incl = wave_inclusive_scan(m0 + m1);
+    const double total = __shfl(incl, 63);
+    const double T = u * total;
+    double lo = __shfl_up(incl, 1);
+    if (lane == 0) lo = 0.0;
+    const double mid = lo + m0;
+    const bool own0 = c0 < NC && lo <= T && T < mid;
+    const bool own1 = c1 < NC && !own0 && mid <= T && T < incl;
+    const unsigned long long mk = __ballot(own0 || own1);
+    int c = -1;
+    double bs = 0.0;
+    if (mk) {
+        const int l = __ffsll((unsigned long long)mk) - 1;
+        const int which = __shfl(own0 ? 0 : 1, l);
+        const double lo_l = __shfl(lo, l), mid_l = __shfl(mid, l);
+        c = 2 * l + which;
+        bs = which == 0 ? lo_l : mid_l;
+    }
+    *owner = c;
+    *base = bs;
+    *T_out = T;
+    return total;
+}
 
 // Search of chunk c for the smallest x with
 // base + sum_{chunk start <= y <= x} w(y) > T, where w is the residual
 // max(0, p*Q - q*P) (RESID) or p itself.  If rounding leaves no such x in
 // the chunk, the last x with w(x) > 0 is taken.  The chunk is re-read with
-// cached loads a few float4s per thread at a time, and the selected segment
-// once more for the final scan (few registers; a rare path).  All threads of
-// the block must call; the token is returned in every thread.
-template <bool VEC, bool RESID>
-__device__ __noinline__ int chunk_draw(const float* prow, const float* qrow, int V, double P, double Q,
-                                       int c, double base, double T)
+// cached loads, one float4 per thread at a time; segment (k, wave) is 256
+// consecutive values and segments are in index order.  All threads of the
+// block must call; the token is returned in every thread.
+template <bool VEC, bool RESID, int NV>
+__device__ __noinline__ int chunk_draw(Row prow, Row qrow, double P, double Q, int c, double base, double T)
 {
-    __shared__ double s_seg[kVec][kWaves];
+    __shared__ double s_seg[NV][kWaves];
     __shared__ int s_ks, s_ws;
     __shared__ double s_base;
     __shared__ int s_x;
@@ -511,11 +667,9 @@ __device__ __noinline__ int chunk_draw(const float* prow, const float* qrow, int
         return t;
     };
 
-    // segment (k, wave) = 256 consecutive values; segments in index order
-#pragma unroll 4
-    for (int k = 0; k < kVec; ++k) {
-        const float4 p4 = load_one<VEC>(prow, V, c, k);
-        const float4 q4 = RESID ? load_one<VEC>(qrow, V, c, k) : p4;
+    for (int k = 0; k < NV; ++k) {
+        const float4 p4 = load_one<VEC, NV>(prow, c, k);
+        const float4 q4 = RESID ? load_one<VEC, NV>(qrow, c, k) : p4;
         const double s = wave_sum(wsum4(p4, q4));
         if (lane == 0) s_seg[k][w] = s;
     }
@@ -524,7 +678,7 @@ __device__ __noinline__ int chunk_draw(const float* prow, const float* qrow, int
         double run = base;
         int ks = -1, ws = 0, lk = 0, lw = 0;
         double bs = base, lb = base;
-        for (int k = 0; k < kVec; ++k) {
+        for (int k = 0; k < NV; ++k) {
             for (int j = 0; j < kWaves; ++j) {
                 const double s = s_seg[k][j];
                 if (s > 0.0) {
@@ -552,8 +706,8 @@ __device__ __noinline__ int chunk_draw(const float* prow, const float* qrow, int
     __syncthreads();
     if (w == s_ws) {
         const int k = s_ks;
-        const float4 p4 = load_one<VEC>(prow, V, c, k);
-        const float4 q4 = RESID ? load_one<VEC>(qrow, V, c, k) : p4;
+        const float4 p4 = load_one<VEC, NV>(prow, c, k);
+        const float4 q4 = RESID ? load_one<VEC, NV>(qrow, c, k) : p4;
         const double incl = wave_inclusive_scan(wsum4(p4, q4));
         double run = __shfl_up(incl, 1);
         if (lane == 0) run = 0.0;
@@ -569,14 +723,14 @@ __device__ __noinline__ int chunk_draw(const float* prow, const float* qrow, int
         const unsigned long long mh = __ballot(hit >= 0);
         if (mh) {
             const int l = __ffsll((unsigned long long)mh) - 1;
-            if (lane == l) s_x = f4_index(c, k) * 4 + hit;
+            if (lane == l) s_x = f4_index<NV>(c, k) * 4 + hit;
         } else {
             const unsigned long long mp = __ballot(lastpos >= 0);
             if (mp) {
                 const int l = 63 - __clzll(mp);
-                if (lane == l) s_x = f4_index(c, k) * 4 + lastpos;
+                if (lane == l) s_x = f4_index<NV>(c, k) * 4 + lastpos;
             } else if (lane == 0) {
-                s_x = f4_index(c, k) * 4;   // unreachable for a segment with mass
+                s_x = f4_index<NV>(c, k) * 4;   // unreachable for a segment with mass
             }
         }
     }
@@ -599,367 +753,431 @@ __device__ __forceinline__ void write_stats(const Args& a, int64_t row, const Ro
     a.stats[row] = s;
 }
 
-// Wave-cooperative: the accept-prefix length of sequence b from the rows'
-// published acceptance bits.
-__device__ __forceinline__ int first_rejection(const Args& a, int b)
+// -------------------------------------------------------- finishing --
+
+struct Outcome {
+    int n;          // accept-prefix length
+    double P, Q;    // masses of row n
+    int arg;        // argmax of row n
+};
+
+// Block-cooperative, run by the block of chunk column 0 after its walk:
+// combine the rows of sequence b in groups of kGroup (wave w takes row
+// g0 + w), take the decisions and, when requested, write the row statistics;
+// without statistics it stops after the group that holds the first
+// rejection.  Uniform result.
+template <bool VEC, bool SAMPLED, int NV, int MROW, int MLAST>
+__device__ Outcome finish_rows(const Args& a, int b)
 {
-    const int lane = threadIdx.x & 63, K = a.K;
-    const int64_t r0 = (int64_t)b * (K + 1);
-    int n = K;
-    for (int base = 0; base < K; base += 64) {
-        const int i = base + lane;
-        const bool rej = i < K && get_i32(&a.rowres[r0 + i].acc) == 0;
-        const unsigned long long m = __ballot(rej);
-        if (m) {
-            n = base + __ffsll((unsigned long long)m) - 1;
-            break;
+    __shared__ int s_rej[kGroup], s_arg[kGroup];
+    __shared__ double s_P[kGroup], s_Q[kGroup];
+    const int K = a.K, V = a.V, NC = a.NC;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    Outcome o{K, 0.0, 0.0, 0};
+    bool done = false;
+    for (int g0 = 0; g0 <= K; g0 += kGroup) {
+        const int nrows = (K + 1 - g0) < kGroup ? (K + 1 - g0) : kGroup;
+        gather_rows<VEC, NV, MROW, MLAST>(a, b, g0, nrows);
+        if (w < nrows) {
+            const int i = g0 + w;
+            const int64_t row = (int64_t)b * (K + 1) + i;
+            const bool pair = SAMPLED && i < K;
+            const RowView rv = i < K ? combine_row<MROW>(w, NC) : combine_row<MLAST>(w, NC);
+            if (lane == 0) {
+                const int tk = i < K ? a.dt[(int64_t)b * K + i] : -1;
+                const bool tin = tk >= 0 && tk < V;
+                const float pt = tin ? a.tp[row * V + tk] : 0.0f;
+                float qt = 0.0f;
+                int rej = 0;
+                if (SAMPLED) {
+                    if (pair) {
+                        qt = tin ? a.dp[((int64_t)b * K + i) * V + tk] : 0.0f;
+                        rej = accepted(a.u[(int64_t)b * (K + 1) + i], pt, qt, rv.P, rv.Q) ? 0 : 1;
+                    }
+                } else {
+                    rej = (i < K && tk != rv.arg) ? 1 : 0;
+                }
+                if (a.stats) write_stats(a, row, rv, pair, pt, qt, i < K);
+                s_rej[w] = rej;
+                s_P[w] = rv.P;
+                s_Q[w] = rv.Q;
+                s_arg[w] = rv.arg;
+            }
         }
+        __syncthreads();
+        if (!done) {
+            int pick = -1;
+            for (int r = 0; r < nrows; ++r)
+                if (pick < 0 && s_rej[r]) pick = r;
+            if (pick < 0 && g0 + nrows == K + 1) pick = nrows - 1;   // row K: every draft accepted
+            if (pick >= 0) {
+                o = Outcome{g0 + pick, s_P[pick], s_Q[pick], s_arg[pick]};
+                done = true;
+            }
+        }
+        __syncthreads();
+        if (done && !a.stats) break;
     }
-    return n;
+    return o;
 }
 
 // ----------------------------------------------------------- greedy --
 
-template <bool VEC>
+template <bool VEC, bool STATS>
 __global__ __launch_bounds__(kThreads) void sv_greedy_kernel(Args a)
 {
-    __shared__ int s_last;
+    constexpr int M = STATS ? (kSP | kAM) : kAM;
     const int NC = a.NC, K = a.K, V = a.V;
-    const unsigned per_seq = (unsigned)(K + 1) * (unsigned)NC;
-    const unsigned item = blockIdx.x;
-    const int b = (int)(item / per_seq);
-    const unsigned r = item - (unsigned)b * per_seq;
-    const int i = (int)(r / (unsigned)NC);
-    const int c = (int)(r - (unsigned)i * (unsigned)NC);
-    const int64_t row = (int64_t)b * (K + 1) + i;
+    const int b = (int)(blockIdx.x / (unsigned)NC);
+    const int c = (int)(blockIdx.x - (unsigned)b * (unsigned)NC);
+    const float* tb = a.tp + (int64_t)b * (K + 1) * V;
+    const int64_t row0 = (int64_t)b * (K + 1);
 
-    float4 pv[kVec];
-    load_chunk<VEC, true>(a.tp + row * V, V, c, pv);
-    const Acc t = thread_stats<false>(pv, pv, V, c);
-    const Acc s = block_reduce<false>(t);
+    // walk rows 0..K of chunk column c; row i+1 loads while row i reduces
+    float4 x0[kVecG], x1[kVecG];
+    load_chunk<VEC, kVecG>(row_of(tb, V), c, x0);
+    for (int i = 0; i <= K; i += 2) {
+        if (i + 1 <= K) load_chunk<VEC, kVecG>(row_of(tb + (int64_t)(i + 1) * V, V), c, x1);
+        publish_part<M>(a, row0 + i, c, block_reduce<M>(thread_stats<M, kVecG>(x0, x0, c)));
+        if (i + 1 > K) break;
+        if (i + 2 <= K) load_chunk<VEC, kVecG>(row_of(tb + (int64_t)(i + 2) * V, V), c, x0);
+        publish_part<M>(a, row0 + i + 1, c, block_reduce<M>(thread_stats<M, kVecG>(x1, x1, c)));
+    }
+    if (c != 0) return;
+
+    const Outcome o = finish_rows<VEC, false, kVecG, M, M>(a, b);
     if (threadIdx.x == 0) {
-        ChunkPart* dst = &a.parts[row * NC + c];
-        put_f64(&dst->sp, s.sp);
-        put_f32(&dst->maxv, s.maxv);
-        put_i32(&dst->arg, s.arg);
-        publish();
-        s_last = count_up(&a.cnt1[row]) == (unsigned)NC - 1u;
+        a.n_out[b] = o.n;
+        a.next_out[b] = o.arg;
     }
-    __syncthreads();
-    if (!s_last || threadIdx.x >= 64) return;
-    // wave 0 of the last block of the row
-    const RowView rv = combine_row<false>(a.parts + row * NC, NC);
-    int last_row = 0;
-    if (threadIdx.x == 0) {
-        put_i32(&a.rowres[row].arg, rv.arg);
-        if (a.stats) {
-            const int tk = i < K ? a.dt[(int64_t)b * K + i] : -1;
-            const bool tin = tk >= 0 && tk < V;
-            write_stats(a, row, rv, false, tin ? a.tp[row * V + tk] : 0.0f, 0.0f, i < K);
-        }
-        publish();
-        last_row = count_up(&a.seqcnt[b]) == (unsigned)K;
-    }
-    last_row = __shfl(last_row, 0);
-    if (!last_row) return;
-    // the sequence's last row: n = first draft that differs from its argmax
-    observe();
-    const int64_t r0 = (int64_t)b * (K + 1);
-    const int lane = threadIdx.x;
-    int n = K;
-    for (int base = 0; base < K; base += 64) {
-        const int j = base + lane;
-        const bool miss = j < K && a.dt[(int64_t)b * K + j] != get_i32(&a.rowres[r0 + j].arg);
-        const unsigned long long m = __ballot(miss);
-        if (m) {
-            n = base + __ffsll((unsigned long long)m) - 1;
-            break;
-        }
-    }
-    int next = 0;
-    if (lane == 0) next = get_i32(&a.rowres[r0 + n].arg);
-    next = __shfl(next, 0);   // the load has completed before any lane zeroes the row results
-    if (lane == 0) {
-        a.n_out[b] = n;
-        a.next_out[b] = next;
-    }
-    zero_sequence(a, b);
 }
 
 // ---------------------------------------------------------- sampled --
 
-// Row ticket: chunk c of target row i of sequence b, with the same chunk of
-// draft row i (the zero chunk for the bonus row i == K, so that both kinds
-// run the same straight-line loads).
-template <bool VEC>
-__device__ __forceinline__ void row_item(const Args& a, int b, int i, int c)
+// The mass partials (sum p, sum q) of one chunk of a row, as loaded by
+// thread t < NC for chunk t, and (thread 0) the inputs of the row's
+// acceptance test.
+struct Poll {
+    unsigned long long sp, sq;
+    float pt, qt, u;
+};
+
+__device__ __forceinline__ Poll poll_issue(const Args& a, int b, int i, int tok)
 {
-    __shared__ int s_last, s_n, s_owner;
-    __shared__ double s_base, s_T, s_P;
-    const int NC = a.NC, K = a.K, V = a.V;
+    Poll p{0ull, 0ull, 0.0f, 0.0f, 0.0f};
+    const int t = threadIdx.x, K = a.K, V = a.V;
     const int64_t row = (int64_t)b * (K + 1) + i;
-    const bool pair = i < K;
-    const float* prow = a.tp + row * V;
-    const float* qrow = pair ? a.dp + ((int64_t)b * K + i) * V : a.zero;
-    const int qV = pair ? V : kChunk;       // the zero operand is one chunk long
-    const int qc = pair ? c : 0;
-
-    float4 pv[kVec], qv[kVec];
-    load_chunk<VEC, true>(prow, V, c, pv);
-    load_chunk<VEC, true>(qrow, qV, qc, qv);
-    const Acc t = thread_stats<true>(pv, qv, V, c);
-    const Acc s = block_reduce<true>(t);
-
-    if (threadIdx.x == 0) {
-        ChunkPart* dst = &a.parts[row * NC + c];
-        put_f64(&dst->sp, s.sp);
-        put_f64(&dst->sq, s.sq);
-        put_f64(&dst->smin, s.smin);
-        put_f32(&dst->maxv, s.maxv);
-        put_i32(&dst->arg, s.arg);
-        publish();
-        s_last = count_up(&a.cnt1[row]) == (unsigned)NC - 1u;
+    if (t < a.NC) {
+        const Part* pp = a.parts + row * a.NC + t;
+        p.sp = get_u64(&pp->sp);
+        p.sq = get_u64(&pp->sq);
     }
-    __syncthreads();
-    if (!s_last) return;
+    if (t == 0) {
+        const bool tin = tok >= 0 && tok < V;
+        p.pt = tin ? a.tp[row * V + tok] : 0.0f;
+        p.qt = tin ? a.dp[((int64_t)b * K + i) * V + tok] : 0.0f;
+        p.u = a.u[row];
+    }
+    return p;
+}
 
-    // last block of the row: combine it, decide its draft's acceptance
-    if (threadIdx.x < 64) {
-        const RowView rv = combine_row<true>(a.parts + row * NC, NC);
-        int last_row = 0;
-        if (threadIdx.x == 0) {
-            const int tk = pair ? a.dt[(int64_t)b * K + i] : -1;
-            const bool tin = tk >= 0 && tk < V;
-            const float pt = tin ? prow[tk] : 0.0f;
-            const float qt = tin ? qrow[tk] : 0.0f;
-            int acc = 1;
-            if (pair) {
-                const double ui = (double)a.u[(int64_t)b * (K + 1) + i];
-                acc = (ui * (double)qt * rv.P < (double)pt * rv.Q) ? 1 : 0;
-            }
-            RowRes* rr = &a.rowres[row];
-            put_f64(&rr->P, rv.P);
-            put_f64(&rr->Q, rv.Q);
-            put_i32(&rr->acc, acc);
-            put_i32(&rr->arg, rv.arg);
-            if (a.stats) write_stats(a, row, rv, pair, pt, qt, pair);
-            publish();
-            last_row = count_up(&a.seqcnt[b]) == (unsigned)K;
-        }
-        last_row = __shfl(last_row, 0);
-        int n = -1;
-        if (last_row) {
-            // the sequence's last row: accept-prefix length, and the bonus
-            // chunk when every draft was accepted
-            observe();
-            n = first_rejection(a, b);
-            if (n == K) {
-                const int64_t rk = (int64_t)b * (K + 1) + K;
-                const double m = threadIdx.x < NC ? get_f64(&a.parts[rk * NC + threadIdx.x].sp) : 0.0;
-                int owner;
-                double base, T;
-                const double uK = (double)a.u[(int64_t)b * (K + 1) + K];
-                const double P = locate_chunk(m, NC, uK, &owner, &base, &T);
-                if (threadIdx.x == 0) {
-                    s_owner = owner;
-                    s_base = base;
-                    s_T = T;
-                    s_P = P;
-                }
+// Block-cooperative: the masses of row i from the polled partials
+// (re-polling the ones that do not carry this call's tag yet) and the
+// acceptance of its draft token.  Returns 0 (accepted), 1 (rejected), or -1
+// when some partial is still missing at the wait bound.  Uniform result.
+__device__ int poll_decide(const Args& a, int b, int i, Poll pl, double* P, double* Q)
+{
+    __shared__ double s_sp[kMaxNC], s_sq[kMaxNC], s_PQ[2];
+    __shared__ int s_rej;
+    const int NC = a.NC, t = threadIdx.x;
+    const unsigned ep = a.epoch;
+    const int64_t row = (int64_t)b * (a.K + 1) + i;
+    bool need = t < NC;
+    const unsigned long long t0 = wall_clock64();
+    for (;;) {
+        bool any = false;
+        if (need) {
+            if (f64_ok(pl.sp, ep) && f64_ok(pl.sq, ep) && !a.force_recompute) {
+                s_sp[t] = f64_of(pl.sp);
+                s_sq[t] = f64_of(pl.sq);
+                need = false;
+            } else {
+                any = true;
             }
         }
-        if (threadIdx.x == 0) s_n = n;
+        if (!__syncthreads_or(any)) break;
+        if (wait_expired(a, t0)) return -1;
+        __builtin_amdgcn_s_sleep(2);
+        if (need) {
+            const Part* pp = a.parts + row * NC + t;
+            pl.sp = get_u64(&pp->sp);
+            pl.sq = get_u64(&pp->sq);
+        }
+    }
+    if (t < 64) {
+        const double p = sum_chunks(s_sp, NC), q = sum_chunks(s_sq, NC);
+        if (t == 0) {
+            s_PQ[0] = p;
+            s_PQ[1] = q;
+            s_rej = accepted(pl.u, pl.pt, pl.qt, p, q) ? 0 : 1;
+        }
     }
     __syncthreads();
-    const int n = s_n;
-    if (n < 0) return;                       // not the sequence's last row
-    if (n < K) {
-        // the residual tickets of this sequence take over
-        if (threadIdx.x == 0) {
-            put_i32(&a.seqinfo[b].n, n);
-            publish();
-            put_u32(&a.seqinfo[b].resolved, 1u);
-        }
-        return;
-    }
-    // every draft accepted: draw the bonus token from p_K
-    const int64_t rk = (int64_t)b * (K + 1) + K;
-    int x = -1;
-    if (s_owner >= 0) x = chunk_draw<VEC, false>(a.tp + rk * V, a.tp + rk * V, V, s_P, 0.0, s_owner, s_base, s_T);
-    if (threadIdx.x == 0) {
-        a.n_out[b] = K;
-        a.next_out[b] = x;
-        put_i32(&a.seqinfo[b].n, K);
-        publish();
-        put_u32(&a.seqinfo[b].resolved, 1u);
+    *P = s_PQ[0];
+    *Q = s_PQ[1];
+    const int rej = s_rej;
+    __syncthreads();
+    return rej;
+}
+
+// Park this thread's share of a row chunk in LDS, and the residual sum of
+// the parked share.
+__device__ __forceinline__ void park(const float4 (&xp)[kVecS], const float4 (&xq)[kVecS])
+{
+#pragma unroll
+    for (int k = 0; k < kVecS; ++k) {
+        lds.parked[k][threadIdx.x] = f32x4{xp[k].x, xp[k].y, xp[k].z, xp[k].w};
+        lds.parked[kVecS + k][threadIdx.x] = f32x4{xq[k].x, xq[k].y, xq[k].z, xq[k].w};
     }
 }
 
-// Residual ticket: chunk c of the residual row of sequence b.
-template <bool VEC>
-__device__ __forceinline__ void resid_item(const Args& a, int b, int c)
+// The order is that of thread_resid_reload (k ascending, one float4 each).
+__device__ __forceinline__ double parked_resid(double P, double Q)
 {
-    __shared__ int s_n, s_last, s_owner, s_resid;
-    __shared__ double s_P, s_Q, s_base, s_T;
-    const int NC = a.NC, K = a.K, V = a.V;
-    if (threadIdx.x == 0) {
-        wait_flag(&a.seqinfo[b].resolved, a.hdr, a.wait_ticks);
-        const int n = get_i32(&a.seqinfo[b].n);
-        s_n = n;
-        if (n < K) {
-            const RowRes* rr = &a.rowres[(int64_t)b * (K + 1) + n];
-            s_P = get_f64(&rr->P);
-            s_Q = get_f64(&rr->Q);
-        }
-    }
-    __syncthreads();
-    const int n = s_n;
-    if (n >= K) {                            // nothing to draw: count, and clean up last
-        if (threadIdx.x == 0) s_last = count_up(&a.cnt2[b]) == (unsigned)NC - 1u;
-        __syncthreads();
-        if (s_last && threadIdx.x < 64) {
-            observe();
-            zero_sequence(a, b);
-        }
-        return;
-    }
-    const int64_t row = (int64_t)b * (K + 1) + n;
-    const float* prow = a.tp + row * V;
-    const float* qrow = a.dp + ((int64_t)b * K + n) * V;
-    const double P = s_P, Q = s_Q;
-
-    // this chunk's residual mass (the rows were streamed moments ago, so
-    // these cached loads hit the Infinity Cache); a quarter chunk at a time
     double w = 0.0;
-#pragma unroll 4
-    for (int k = 0; k < kVec; ++k) {
-        const float4 p4 = load_one<VEC>(prow, V, c, k), q4 = load_one<VEC>(qrow, V, c, k);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w += resid(comp(p4, e), comp(q4, e), P, Q);
+    for (int k = 0; k < kVecS; ++k) {
+        const f32x4 p = lds.parked[k][threadIdx.x], q = lds.parked[kVecS + k][threadIdx.x];
+        w += resid_f4(make_float4(p.x, p.y, p.z, p.w), make_float4(q.x, q.y, q.z, q.w), P, Q);
     }
-    w = block_sum(w);
-    if (threadIdx.x == 0) {
-        put_f64(&a.wpart[(int64_t)b * NC + c], w);
-        publish();
-        s_last = count_up(&a.cnt2[b]) == (unsigned)NC - 1u;
+    return w;
+}
+
+// Block-cooperative: the residual chunk masses of row n (published by the
+// walking blocks) into m[0..NC); missing ones, and ones published as NaN
+// (their block could not decide), are recomputed.
+template <bool VEC>
+__device__ void gather_resid(const Args& a, int b, int n, double P, double Q, double* m)
+{
+    __shared__ unsigned long long s_miss[2];
+    const int NC = a.NC, K = a.K, V = a.V;
+    const unsigned ep = a.epoch;
+    const unsigned long long* wp = a.wpart + ((int64_t)b * K + n) * NC;
+    const int c = threadIdx.x;
+    bool need = c < NC, redo = false;
+    const unsigned long long t0 = wall_clock64();
+    for (;;) {
+        bool any = false;
+        if (need) {
+            const unsigned long long wv = get_u64(&wp[c]);
+            if (f64_ok(wv, ep) && !a.force_recompute) {
+                m[c] = f64_of(wv);
+                need = false;
+                if (m[c] != m[c]) redo = true;   // published as "recompute"
+            } else {
+                any = true;
+            }
+        }
+        if (!__syncthreads_or(any)) break;
+        if (wait_expired(a, t0)) break;
+        __builtin_amdgcn_s_sleep(2);
+    }
+    if (threadIdx.x < 2) s_miss[threadIdx.x] = 0ull;
+    __syncthreads();
+    if (need || redo) atomicOr(&s_miss[c >> 6], 1ull << (c & 63));   // LDS
+    __syncthreads();
+    const Row prow = row_of(a.tp + ((int64_t)b * (K + 1) + n) * V, V);
+    const Row qrow = row_of(a.dp + ((int64_t)b * K + n) * V, V);
+    for (int h = 0; h < 2; ++h) {
+        unsigned long long mk = s_miss[h];
+        while (mk) {
+            const int cc = h * 64 + __ffsll((unsigned long long)mk) - 1;
+            mk &= mk - 1;
+            const double w = block_sum(thread_resid_reload<VEC, kVecS>(prow, qrow, cc, P, Q));
+            if (threadIdx.x == 0) {
+                m[cc] = strip8(w);
+                put_u32(&a.hdr->slow_path, 1u);
+            }
+        }
     }
     __syncthreads();
-    if (!s_last) return;
+}
 
-    // last residual ticket: locate the chunk of u_K * W and draw there
-    if (threadIdx.x < 64) {
-        observe();
-        const double uK = (double)a.u[(int64_t)b * (K + 1) + K];
-        const double m = threadIdx.x < NC ? get_f64(&a.wpart[(int64_t)b * NC + threadIdx.x]) : 0.0;
-        int owner;
-        double base, T;
-        const double W = locate_chunk(m, NC, uK, &owner, &base, &T);
-        int rs = 1;
-        if (!(W > 0.0)) {
-            // rounding left no residual mass: draw from p_n itself
-            const double mp = threadIdx.x < NC ? get_f64(&a.parts[row * NC + threadIdx.x].sp) : 0.0;
-            locate_chunk(mp, NC, uK, &owner, &base, &T);
-            rs = 0;
+// Search state of a walking block (the same in every block of a sequence,
+// since every block takes the same decisions from the same masses).
+enum : int { kSearching = -1, kLost = -2 };
+
+template <bool VEC, bool STATS>
+__global__ __launch_bounds__(kThreads, 4) void sv_sample_kernel(Args a)
+{
+    constexpr int MP = STATS ? (kSP | kSQ | kSMIN | kAM) : (kSP | kSQ);   // rows 0..K-1
+    constexpr int MB = STATS ? (kSP | kAM) : kSP;                        // bonus row K
+    __shared__ double s_m[kMaxNC];
+    __shared__ int s_owner, s_resid;
+    __shared__ double s_base, s_T;
+    const int NC = a.NC, K = a.K, V = a.V;
+    const int b = (int)(blockIdx.x / (unsigned)NC);
+    const int c = (int)(blockIdx.x - (unsigned)b * (unsigned)NC);
+    const float* tb = a.tp + (int64_t)b * (K + 1) * V;
+    const float* db = a.dp + (int64_t)b * K * V;
+    const int64_t row0 = (int64_t)b * (K + 1);
+
+    // Walk rows 0..K of chunk column c.  At step i row i is in registers
+    // (xp, xq) and row i+1 loads into (yp, yq).  While no draft has been
+    // rejected yet, row i-1 waits in LDS for its decision: its partials were
+    // published by the sibling blocks a step ago and are polled (with the
+    // inputs of its acceptance test) before row i+1's loads are issued, so,
+    // loads returning in order, they arrive while those loads are in flight.
+    // The first rejected row n gets its chunk's residual mass published;
+    // after it the walk only streams and publishes partials.
+    int state = K > 0 ? kSearching : 0;   // kSearching, kLost, or the decided n
+    double Pn = 0.0, Qn = 0.0;
+    int tok = -1;                          // draft token of the pending row (thread 0)
+    float4 xp[kVecS], xq[kVecS], yp[kVecS], yq[kVecS];
+    load_chunk<VEC, kVecS>(row_of(tb, V), c, xp);
+    load_chunk<VEC, kVecS>(row_of(db, K > 0 ? V : 0), c, xq);
+
+    // decide row j (parked) from its poll; publish its residual if rejected
+    auto decide = [&](int j, const Poll& pl) {
+        double P, Q;
+        const int rej = poll_decide(a, b, j, pl, &P, &Q);
+        if (rej < 0) {
+            // masses missing: leave the decision to the finisher, marking the
+            // residuals of every row from j on as "recompute"
+            state = kLost;
+            if (threadIdx.x == 0)
+                for (int r = j; r < K; ++r)
+                    put_u64(&a.wpart[((int64_t)b * K + r) * NC + c], tag_f64(__builtin_nan(""), a.epoch));
+        } else if (rej) {
+            state = j;
+            Pn = P;
+            Qn = Q;
+            const double w = block_sum(parked_resid(P, Q));
+            if (threadIdx.x == 0) put_u64(&a.wpart[((int64_t)b * K + j) * NC + c], tag_f64(w, a.epoch));
         }
+    };
+
+    for (int i = 0; i < K; ++i) {
+        Poll pl{0ull, 0ull, 0.0f, 0.0f, 0.0f};
+        const bool pending = i > 0 && state == kSearching;
+        if (pending) pl = poll_issue(a, b, i - 1, tok);
+        if (threadIdx.x == 0 && state == kSearching) tok = a.dt[(int64_t)b * K + i];   // row i's token, for step i+1
+        __builtin_amdgcn_sched_barrier(0);
+        const bool next_pair = i + 1 < K;
+        load_chunk<VEC, kVecS>(row_of(tb + (int64_t)(i + 1) * V, V), c, yp);
+        load_chunk<VEC, kVecS>(row_of(db + (next_pair ? (int64_t)(i + 1) * V : 0), next_pair ? V : 0), c, yq);
+        __builtin_amdgcn_sched_barrier(0);
+        publish_part<MP>(a, row0 + i, c, block_reduce<MP>(thread_stats<MP, kVecS>(xp, xq, c)));
+        if (pending) decide(i - 1, pl);
+        if (state == kSearching) park(xp, xq);
+#pragma unroll
+        for (int k = 0; k < kVecS; ++k) {
+            xp[k] = yp[k];
+            xq[k] = yq[k];
+        }
+    }
+    {
+        Poll pl{0ull, 0ull, 0.0f, 0.0f, 0.0f};
+        const bool pending = K > 0 && state == kSearching;
+        if (pending) pl = poll_issue(a, b, K - 1, tok);
+        publish_part<MB>(a, row0 + K, c, block_reduce<MB>(thread_stats<MB, kVecS>(xp, xp, c)));
+        if (pending) decide(K - 1, pl);
+        if (state == kSearching) state = K;   // every draft accepted
+    }
+    if (c != 0) return;
+
+    // finish sequence b: the decisions if this block could not take them
+    // (or the row statistics), then the final draw
+    int n = state;
+    if (STATS || n == kLost) {
+        const Outcome o = finish_rows<VEC, true, kVecS, MP, MB>(a, b);
+        n = o.n;
+        Pn = o.P;
+        Qn = o.Q;
+    }
+    const double uK = (double)a.u[row0 + K];
+    const Row prow = row_of(a.tp + (row0 + n) * V, V);
+    const Row qrow = n < K ? row_of(a.dp + ((int64_t)b * K + n) * V, V) : prow;
+    if (n < K) gather_resid<VEC>(a, b, n, Pn, Qn, s_m);
+    if (threadIdx.x < 64) {
+        int owner = -1;
+        double base = 0.0, T = 0.0, W = 0.0;
+        if (n < K) W = locate_chunk(s_m, NC, uK, &owner, &base, &T);
         if (threadIdx.x == 0) {
             s_owner = owner;
             s_base = base;
             s_T = T;
-            s_resid = rs;
+            s_resid = (n < K && W > 0.0) ? 1 : 0;
         }
     }
     __syncthreads();
+    if (!s_resid) {
+        // bonus draw from p_K, or (rounding only) a rejection that left no
+        // residual mass: draw from p_n, located by its target chunk masses
+        if (n < K)
+            gather_rows<VEC, kVecS, kSP, kSP>(a, b, n, 1);
+        else
+            gather_rows<VEC, kVecS, kSP, MB>(a, b, n, 1);
+        if (threadIdx.x < 64) {
+            int owner;
+            double base, T;
+            locate_chunk(lds.g.sp[0], NC, uK, &owner, &base, &T);
+            if (threadIdx.x == 0) {
+                s_owner = owner;
+                s_base = base;
+                s_T = T;
+            }
+        }
+        __syncthreads();
+    }
     int x = -1;
     if (s_owner >= 0)
-        x = s_resid ? chunk_draw<VEC, true>(prow, qrow, V, P, Q, s_owner, s_base, s_T)
-                    : chunk_draw<VEC, false>(prow, prow, V, P, Q, s_owner, s_base, s_T);
-    if (threadIdx.x < 64) {
-        if (threadIdx.x == 0) {
-            a.n_out[b] = n;
-            a.next_out[b] = x;
-        }
-        zero_sequence(a, b);
-    }
-}
-
-// Ticket order: sequences in order; row tickets of sequence r are followed
-// by the residual tickets of sequence r - lag.
-struct Ticket {
-    int kind;                // 0 row, 1 residual
-    int b, i, c;
-};
-
-__device__ __forceinline__ Ticket decode(const Args& a, unsigned tk)
-{
-    const unsigned NC = (unsigned)a.NC, P1 = (unsigned)(a.K + 1) * NC, RI = NC;
-    const unsigned D = (unsigned)a.lag, Bs = (unsigned)a.B;
-    const unsigned partA = D * P1, partB = (Bs - D) * (P1 + RI);
-    Ticket t{};
-    if (tk < partA) {
-        const unsigned r = tk / P1, off = tk - r * P1;
-        t = Ticket{0, (int)r, (int)(off / NC), (int)(off % NC)};
-    } else if (tk < partA + partB) {
-        const unsigned x = tk - partA, r = D + x / (P1 + RI), off = x % (P1 + RI);
-        if (off < P1)
-            t = Ticket{0, (int)r, (int)(off / NC), (int)(off % NC)};
-        else
-            t = Ticket{1, (int)(r - D), 0, (int)(off - P1)};
-    } else {
-        const unsigned x = tk - partA - partB;
-        t = Ticket{1, (int)(Bs - D + x / RI), 0, (int)(x % RI)};
-    }
-    return t;
-}
-
-template <bool VEC>
-__global__ __launch_bounds__(kThreads, 4) void sv_sample_kernel(Args a)
-{
-    __shared__ unsigned s_ticket;
-    for (;;) {
-        // one atomic hands out kTicketBatch consecutive tickets: the counter
-        // is the one hot address of the launch.  A block processes its batch
-        // in order; the progress argument holds because a block waits only on
-        // a sequence whose row tickets all precede its current ticket.
-        if (threadIdx.x == 0) s_ticket = a.batch * count_up(&a.hdr->ticket);
-        __syncthreads();
-        const unsigned tk0 = __builtin_amdgcn_readfirstlane(s_ticket);
-        __syncthreads();
-        if (tk0 >= a.total) break;
-        for (unsigned tk = tk0; tk < tk0 + a.batch && tk < a.total; ++tk) {
-            const Ticket t = decode(a, tk);
-            if (t.kind == 0)
-                row_item<VEC>(a, t.b, t.i, t.c);
-            else
-                resid_item<VEC>(a, t.b, t.c);
-            __syncthreads();
-        }
-    }
+        x = s_resid ? chunk_draw<VEC, true, kVecS>(prow, qrow, Pn, Qn, s_owner, s_base, s_T)
+                    : chunk_draw<VEC, false, kVecS>(prow, prow, Pn, Qn, s_owner, s_base, s_T);
     if (threadIdx.x == 0) {
-        if (count_up(&a.hdr->exit_count) == gridDim.x - 1u) {
-            put_u32(&a.hdr->ticket, 0u);     // every block has taken its last ticket
-            put_u32(&a.hdr->exit_count, 0u);
-        }
+        a.n_out[b] = n;
+        a.next_out[b] = x;
     }
 }
 
 __global__ void sv_fill_zero_kernel(uint4* p, size_t n16)
 {
-    const size_t stride = (size_t)gridDim.x * blockDim.x;
-    for (size_t j = (size_t)blockIdx.x * blockDim.x + threadIdx.x; j < n16; j += stride)
-        p[j] = make_uint4(0u, 0u, 0u, 0u);
+    const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+    for (size_t j = (size_t)blockIdx.x * blockDim.x + threadIdx.x; j < n16; j += (size_t)gridDim.x * blockDim.x)
+        p[j] = z;
 }
 
 // ------------------------------------------------------------- host --
 
 struct DevInfo {
-    int cus = 0;
     int wall_khz = 0;
-    int occ[2] = {0, 0};     // resident sampled blocks per CU: scalar, vector path
     bool ok = false;
 };
 
 std::mutex g_mu;
 DevInfo g_dev[64];
+struct WsState {
+    unsigned calls = 0;      // calls since the last clear (tags 1..calls are in use)
+    size_t bytes = 0;        // largest extent of the workspace seen
+};
+std::unordered_map<const void*, WsState> g_ws;
+
+struct Tuning {
+    double poll_us = kPollMicroseconds;
+    int force_recompute = 0;
+};
+
+// Read at every call: SV_VERIFY_POLL_US bounds a wait for a sibling's
+// partials; SV_VERIFY_FORCE_RECOMPUTE=1 makes every reader recompute what it
+// gathers (a test hook for the recompute path).
+Tuning tuning()
+{
+    Tuning r;
+    if (const char* s = std::getenv("SV_VERIFY_POLL_US")) r.poll_us = std::atof(s);
+    if (const char* s = std::getenv("SV_VERIFY_FORCE_RECOMPUTE")) r.force_recompute = std::atoi(s) != 0;
+    if (!(r.poll_us >= 0.0) || r.poll_us > 1e7) r.poll_us = kPollMicroseconds;
+    return r;
+}
 
 sv_status device_info(DevInfo* out)
 {
@@ -968,20 +1186,10 @@ sv_status device_info(DevInfo* out)
     std::lock_guard<std::mutex> lk(g_mu);
     DevInfo& d = g_dev[dev];
     if (!d.ok) {
-        int cus = 0, o0 = 0, o1 = 0;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-            return SV_ERR_HIP;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o0, sv_sample_kernel<false>, kThreads, 0) != hipSuccess)
-            return SV_ERR_HIP;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o1, sv_sample_kernel<true>, kThreads, 0) != hipSuccess)
-            return SV_ERR_HIP;
         int khz = 0;
         if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz <= 0)
             khz = 100000;   // gfx9 wall clock: 100 MHz
         d.wall_khz = khz;
-        d.cus = cus;
-        d.occ[0] = o0;
-        d.occ[1] = o1;
         d.ok = true;
     }
     *out = d;
@@ -994,31 +1202,62 @@ sv_status check_sizes(int32_t B, int32_t K, int32_t V)
 {
     if (B < 0 || K < 0 || V < 1) return SV_ERR_INVALID_ARG;
     if (V > SV_MAX_V || K > SV_MAX_K) return SV_ERR_UNSUPPORTED;
-    const uint64_t NC = ((uint64_t)V + kChunk - 1) / kChunk;
-    if ((uint64_t)B * (uint64_t)(K + 2) * NC >= (1ull << 31)) return SV_ERR_UNSUPPORTED;
+    const uint64_t NC = ((uint64_t)V + kChunkS - 1) / kChunkS;   // the larger chunk count
+    if ((uint64_t)B * (uint64_t)(K + 1) * NC >= (1ull << 31)) return SV_ERR_UNSUPPORTED;
     return SV_OK;
 }
 
-Args make_args(void* ws, int32_t B, int32_t K, int32_t V)
+sv_status launch_fill(void* ws, size_t bytes, hipStream_t s)
+{
+    const size_t n16 = bytes / 16;
+    if (n16 == 0) return SV_OK;
+    size_t blocks = (n16 + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(sv_fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s, static_cast<uint4*>(ws), n16);
+    return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+// The tag of this call on `ws` (1..kEpochs).  Each tag is used once between
+// clears: the first call on a workspace the library has not seen, and every
+// call after kEpochs tags have been used, clears the whole extent of the
+// workspace seen so far on `s` first, so no word left by an earlier call can
+// carry a tag in use.
+sv_status next_epoch(void* ws, size_t bytes, hipStream_t s, unsigned* ep)
+{
+    bool clear = false;
+    size_t extent = 0;
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        auto it = g_ws.find(ws);
+        if (it == g_ws.end()) {
+            it = g_ws.emplace(ws, WsState{}).first;
+            it->second.calls = kEpochs;   // unknown contents: clear first
+        }
+        WsState& st = it->second;
+        if (bytes > st.bytes) st.bytes = bytes;
+        if (st.calls >= kEpochs) {
+            st.calls = 0;
+            clear = true;
+        }
+        *ep = ++st.calls;
+        extent = st.bytes;
+    }
+    return clear ? launch_fill(ws, extent, s) : SV_OK;
+}
+
+Args make_args(void* ws, int32_t B, int32_t K, int32_t V, bool sampled)
 {
     Args a{};
-    const int NC = (V + kChunk - 1) / kChunk;
-    const Layout L = make_layout(B, K, NC);
+    const int NC = (V + chunk_of(sampled) - 1) / chunk_of(sampled);
+    const Layout L = make_layout(B, K, NC, sampled);
     unsigned char* w = static_cast<unsigned char*>(ws);
     a.hdr = reinterpret_cast<Header*>(w + L.hdr);
-    a.cnt1 = reinterpret_cast<unsigned*>(w + L.cnt1);
-    a.cnt2 = reinterpret_cast<unsigned*>(w + L.cnt2);
-    a.seqcnt = reinterpret_cast<unsigned*>(w + L.seqcnt);
-    a.seqinfo = reinterpret_cast<SeqInfo*>(w + L.seqinfo);
-    a.rowres = reinterpret_cast<RowRes*>(w + L.rowres);
-    a.parts = reinterpret_cast<ChunkPart*>(w + L.parts);
-    a.wpart = reinterpret_cast<double*>(w + L.wpart);
-    a.zero = reinterpret_cast<const float*>(w + L.zero);
+    a.parts = reinterpret_cast<Part*>(w + L.parts);
+    a.wpart = reinterpret_cast<unsigned long long*>(w + L.wpart);
     a.B = B;
     a.K = K;
     a.V = V;
     a.NC = NC;
-    a.lag = B < kLag ? B : kLag;
     return a;
 }
 
@@ -1028,22 +1267,22 @@ extern "C" {
 
 size_t sv_workspace_size(int32_t B, int32_t K, int32_t V, int32_t sampled)
 {
-    (void)sampled;   // both modes share one layout
     if (check_sizes(B, K, V) != SV_OK) return 0;
-    const int NC = (V + kChunk - 1) / kChunk;
-    return make_layout(B, K, NC).total;
+    const bool s = sampled != 0;
+    const int NC = (V + chunk_of(s) - 1) / chunk_of(s);
+    return make_layout(B, K, NC, s).total;
 }
 
 sv_status sv_workspace_init(void* workspace, size_t workspace_bytes, void* stream)
 {
     if (!workspace || !aligned(workspace, 16)) return SV_ERR_WORKSPACE;
-    const size_t n16 = workspace_bytes / 16;
-    if (n16 == 0) return SV_OK;
-    size_t blocks = (n16 + 255) / 256;
-    if (blocks > 4096) blocks = 4096;
-    hipLaunchKernelGGL(sv_fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0,
-                       static_cast<hipStream_t>(stream), static_cast<uint4*>(workspace), n16);
-    return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        WsState& st = g_ws[workspace];
+        st.calls = 0;
+        st.bytes = workspace_bytes;
+    }
+    return launch_fill(workspace, workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
 sv_status sv_verify_greedy_batched(const float* target_probs, const int32_t* draft_tokens,
@@ -1062,20 +1301,31 @@ sv_status sv_verify_greedy_batched(const float* target_probs, const int32_t* dra
         return SV_ERR_INVALID_ARG;
     if (!workspace || !aligned(workspace, 16) || workspace_bytes < sv_workspace_size(B, K, V, 0))
         return SV_ERR_WORKSPACE;
-    Args a = make_args(workspace, B, K, V);
+    DevInfo d;
+    st = device_info(&d);
+    if (st != SV_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    Args a = make_args(workspace, B, K, V, false);
+    st = next_epoch(workspace, workspace_bytes, s, &a.epoch);
+    if (st != SV_OK) return st;
     a.tp = target_probs;
     a.dt = draft_tokens;
     a.n_out = n_accepted;
     a.next_out = next_token;
     a.stats = stats;
-    a.total = (unsigned)((uint64_t)B * (uint64_t)(K + 1) * (uint64_t)a.NC);
+    const Tuning tu = tuning();
+    a.force_recompute = tu.force_recompute;
+    a.poll_ticks = (unsigned long long)(tu.poll_us * 1e-3 * (double)d.wall_khz);
     const bool vec = (V % 4 == 0) && aligned(target_probs, 16);
-    const dim3 grid(a.total), block(kThreads);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (vec)
-        hipLaunchKernelGGL(sv_greedy_kernel<true>, grid, block, 0, s, a);
+    const dim3 grid((unsigned)((uint64_t)B * (uint64_t)a.NC)), block(kThreads);
+    if (vec && stats)
+        hipLaunchKernelGGL((sv_greedy_kernel<true, true>), grid, block, 0, s, a);
+    else if (vec)
+        hipLaunchKernelGGL((sv_greedy_kernel<true, false>), grid, block, 0, s, a);
+    else if (stats)
+        hipLaunchKernelGGL((sv_greedy_kernel<false, true>), grid, block, 0, s, a);
     else
-        hipLaunchKernelGGL(sv_greedy_kernel<false>, grid, block, 0, s, a);
+        hipLaunchKernelGGL((sv_greedy_kernel<false, false>), grid, block, 0, s, a);
     return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
@@ -1101,7 +1351,10 @@ sv_status sv_verify_sample_batched(const float* target_probs, const float* draft
     DevInfo d;
     st = device_info(&d);
     if (st != SV_OK) return st;
-    Args a = make_args(workspace, B, K, V);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    Args a = make_args(workspace, B, K, V, true);
+    st = next_epoch(workspace, workspace_bytes, s, &a.epoch);
+    if (st != SV_OK) return st;
     a.tp = target_probs;
     a.dp = draft_probs;
     a.dt = draft_tokens;
@@ -1109,21 +1362,19 @@ sv_status sv_verify_sample_batched(const float* target_probs, const float* draft
     a.n_out = n_accepted;
     a.next_out = next_token;
     a.stats = stats;
-    a.wait_ticks = (unsigned long long)(kWaitSeconds * 1000.0 * (double)d.wall_khz);
-    a.total = (unsigned)((uint64_t)B * (uint64_t)(K + 2) * (uint64_t)a.NC);   // row + residual tickets
+    const Tuning tu = tuning();
+    a.force_recompute = tu.force_recompute;
+    a.poll_ticks = (unsigned long long)(tu.poll_us * 1e-3 * (double)d.wall_khz);
     const bool vec = (V % 4 == 0) && aligned(target_probs, 16) && (K == 0 || aligned(draft_probs, 16));
-    const int occ = d.occ[vec ? 1 : 0];
-    const uint64_t resident = (uint64_t)(occ > 0 ? occ : 1) * (uint64_t)d.cus;
-    // batch tickets only when there are many per resident block: on small
-    // launches a batch would serialise work that could run side by side
-    a.batch = a.total >= 16u * resident ? kTicketBatch : (a.total >= 4u * resident ? 2u : 1u);
-    const uint64_t blocks = (a.total + a.batch - 1) / a.batch;
-    const unsigned grid = (unsigned)(resident < blocks ? resident : blocks);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (vec)
-        hipLaunchKernelGGL(sv_sample_kernel<true>, dim3(grid), dim3(kThreads), 0, s, a);
+    const dim3 grid((unsigned)((uint64_t)B * (uint64_t)a.NC)), block(kThreads);
+    if (vec && stats)
+        hipLaunchKernelGGL((sv_sample_kernel<true, true>), grid, block, 0, s, a);
+    else if (vec)
+        hipLaunchKernelGGL((sv_sample_kernel<true, false>), grid, block, 0, s, a);
+    else if (stats)
+        hipLaunchKernelGGL((sv_sample_kernel<false, true>), grid, block, 0, s, a);
     else
-        hipLaunchKernelGGL(sv_sample_kernel<false>, dim3(grid), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((sv_sample_kernel<false, false>), grid, block, 0, s, a);
     return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
