@@ -22,7 +22,8 @@
 //     its chunk's residual mass sum max(0, p*Q - q*P) from the row-i data it
 //     still holds in registers.  No row is read twice: the final draw
 //     re-reads a single chunk.
-//   * the block of chunk column 0 finishes the sequence after its walk: it
+//   * one block of each sequence (its column rotates with b, so that the
+//     work spreads over the XCDs) finishes the sequence after its walk: it
 //     combines the rows (in chunk order), takes the acceptance decisions and
 //     the accept-prefix length n, and emits the next token -- argmax of row n
 //     (greedy), or an inverse-CDF draw over the residual of row n or over
@@ -349,11 +350,68 @@ __device__ __forceinline__ double thread_resid_reload(Row prow, Row qrow, int c,
     return w;
 }
 
+// Wave-level exchanges through DPP (data-parallel primitives: a lane reads
+// another lane of its 16-lane row inside a VALU move, no LDS round trip).
+// Controls: swap within pairs, swap pairs within quads, mirror within
+// halves of a row, mirror within a row.  After the four steps every lane of
+// a row holds the row's result (each step combines a lane with its partner,
+// and the two partners compute the same commutative sum or merge).
+constexpr int kDppPairs = 0xB1, kDppQuads = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i32(int v)
+{
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v)
+{
+    const long long bits = __double_as_longlong(v);
+    const int lo = dpp_i32<CTRL>((int)bits), hi = dpp_i32<CTRL>((int)(bits >> 32));
+    return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+__device__ __forceinline__ double lane_f64(double v, int l)
+{
+    const long long bits = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_readlane((int)bits, l), hi = __builtin_amdgcn_readlane((int)(bits >> 32), l);
+    return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+
+// Sum over the wave (all 64 lanes active), the same value in every lane:
+// row sums by DPP, then the four row sums in row order.
 __device__ __forceinline__ double wave_sum(double v)
 {
+    v += dpp_f64<kDppPairs>(v);
+    v += dpp_f64<kDppQuads>(v);
+    v += dpp_f64<kDppHalfMirror>(v);
+    v += dpp_f64<kDppMirror>(v);
+    return (lane_f64(v, 0) + lane_f64(v, 16)) + (lane_f64(v, 32) + lane_f64(v, 48));
+}
+
+template <int CTRL>
+__device__ __forceinline__ void argmax_step(float& v, int& i)
+{
+    const float ov = __int_as_float(dpp_i32<CTRL>(__float_as_int(v)));
+    const int oi = dpp_i32<CTRL>(i);
+    argmax_merge(v, i, ov, oi);
+}
+
+// (value, index) maximum over the wave (all 64 lanes active), the same in
+// every lane.
+__device__ __forceinline__ void wave_argmax(float& v, int& i)
+{
+    argmax_step<kDppPairs>(v, i);
+    argmax_step<kDppQuads>(v, i);
+    argmax_step<kDppHalfMirror>(v, i);
+    argmax_step<kDppMirror>(v, i);
+    float bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    int bi = __builtin_amdgcn_readlane(i, 0);
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-    return v;   // identical in every lane (each level adds the same pair)
+    for (int r = 1; r < 4; ++r)
+        argmax_merge(bv, bi, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16 * r)),
+                     __builtin_amdgcn_readlane(i, 16 * r));
+    v = bv;
+    i = bi;
 }
 
 __device__ __forceinline__ double wave_inclusive_scan(double v)
@@ -375,17 +433,10 @@ __device__ __forceinline__ Acc block_reduce(Acc a)
     __shared__ double s_sp[kWaves], s_sq[kWaves], s_sm[kWaves];
     __shared__ float s_v[kWaves];
     __shared__ int s_i[kWaves];
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-        if constexpr ((M & kSP) != 0) a.sp += __shfl_xor(a.sp, off);
-        if constexpr ((M & kSQ) != 0) a.sq += __shfl_xor(a.sq, off);
-        if constexpr ((M & kSMIN) != 0) a.smin += __shfl_xor(a.smin, off);
-        if constexpr ((M & kAM) != 0) {
-            const float ov = __shfl_xor(a.maxv, off);
-            const int oi = __shfl_xor(a.arg, off);
-            argmax_merge(a.maxv, a.arg, ov, oi);
-        }
-    }
+    if constexpr ((M & kSP) != 0) a.sp = wave_sum(a.sp);
+    if constexpr ((M & kSQ) != 0) a.sq = wave_sum(a.sq);
+    if constexpr ((M & kSMIN) != 0) a.smin = wave_sum(a.smin);
+    if constexpr ((M & kAM) != 0) wave_argmax(a.maxv, a.arg);
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     if (lane == 0) {
         s_sp[w] = a.sp;
@@ -457,26 +508,31 @@ __device__ __forceinline__ void publish_part(const Args& a, int64_t row, int c, 
 
 // ------------------------------------------------------ gathering --
 
-// The gathered partials of up to kGroup rows of one sequence.
+// The gathered partials of up to kGroup rows of one sequence (LDS), for at
+// most NCMAX chunks per row.
+template <int NCMAX>
 struct Gathered {
-    double sp[kGroup][kMaxNC];
-    double sq[kGroup][kMaxNC];
-    double smin[kGroup][kMaxNC];
-    unsigned long long am[kGroup][kMaxNC];
+    static constexpr int kCap = NCMAX;
+    double sp[kGroup][NCMAX];
+    double sq[kGroup][NCMAX];
+    double smin[kGroup][NCMAX];
+    unsigned long long am[kGroup][NCMAX];
 };
 
 // LDS of a block: while it walks its chunk column, the chunk of the row
 // whose decision is pending (target float4s, then draft float4s; each thread
 // touches only its own column, so no barrier guards it); when it finishes a
 // sequence, the gathered partials.
-union LdsArea {
+union SampleLds {
     f32x4 parked[2 * kVecS][kThreads];
-    Gathered g;
+    Gathered<kMaxNC> g;
 };
-__shared__ LdsArea lds;
+__shared__ SampleLds lds;
+// The greedy kernel's rows have at most SV_MAX_V / kChunkG chunks.
+__shared__ Gathered<SV_MAX_V / kChunkG> lds_greedy;
 
-template <int M>
-__device__ __forceinline__ bool part_ok(const Part* pp, unsigned ep, int r, int c, bool store)
+template <int M, class G>
+__device__ __forceinline__ bool part_ok(G& g, const Part* pp, unsigned ep, int r, int c, bool store)
 {
     const unsigned long long wsp = (M & kSP) ? get_u64(&pp->sp) : 0ull;
     const unsigned long long wsq = (M & kSQ) ? get_u64(&pp->sq) : 0ull;
@@ -485,39 +541,39 @@ __device__ __forceinline__ bool part_ok(const Part* pp, unsigned ep, int r, int 
     const bool ok = (!(M & kSP) || f64_ok(wsp, ep)) && (!(M & kSQ) || f64_ok(wsq, ep)) &&
                     (!(M & kSMIN) || f64_ok(wsm, ep)) && (!(M & kAM) || am_ok(wam, ep));
     if (ok && store) {
-        lds.g.sp[r][c] = f64_of(wsp);
-        lds.g.sq[r][c] = f64_of(wsq);
-        lds.g.smin[r][c] = f64_of(wsm);
-        lds.g.am[r][c] = wam;
+        g.sp[r][c] = f64_of(wsp);
+        g.sq[r][c] = f64_of(wsq);
+        g.smin[r][c] = f64_of(wsm);
+        g.am[r][c] = wam;
     }
     return ok;
 }
 
-template <bool VEC, int M, int NV>
-__device__ void recompute_part(const Args& a, Row prow, Row qrow, int r, int c)
+template <bool VEC, int M, int NV, class G>
+__device__ void recompute_part(G& g, const Args& a, Row prow, Row qrow, int r, int c)
 {
     const Acc s = block_reduce<M>(thread_stats_reload<VEC, M, NV>(prow, qrow, c));
     if (threadIdx.x == 0) {
-        lds.g.sp[r][c] = strip8(s.sp);
-        lds.g.sq[r][c] = strip8(s.sq);
-        lds.g.smin[r][c] = strip8(s.smin);
-        lds.g.am[r][c] = tag_am(s.maxv, s.arg, a.epoch);
+        g.sp[r][c] = strip8(s.sp);
+        g.sq[r][c] = strip8(s.sq);
+        g.smin[r][c] = strip8(s.smin);
+        g.am[r][c] = tag_am(s.maxv, s.arg, a.epoch);
         put_u32(&a.hdr->slow_path, 1u);
     }
 }
 
 // Block-cooperative: read the partials of rows row0 .. row0 + nrows - 1 of
-// sequence b (rows numbered within the sequence) into lds.g: fields MROW of
+// sequence b (rows numbered within the sequence) into g: fields MROW of
 // rows below K and MLAST of row K.  Partials that do not carry this call's
 // tag within the wait bound are recomputed from the inputs.
-template <bool VEC, int NV, int MROW, int MLAST>
-__device__ void gather_rows(const Args& a, int b, int row0, int nrows)
+template <bool VEC, int NV, int MROW, int MLAST, class G>
+__device__ void gather_rows(G& g, const Args& a, int b, int row0, int nrows)
 {
     __shared__ unsigned long long s_miss[kGroup][2];
     const int NC = a.NC, K = a.K, V = a.V;
     const unsigned ep = a.epoch;
     const int n_ent = nrows * NC;
-    constexpr int kPer = (kGroup * kMaxNC + kThreads - 1) / kThreads;   // entries per thread
+    constexpr int kPer = (kGroup * G::kCap + kThreads - 1) / kThreads;   // entries per thread
     bool need[kPer];
 #pragma unroll
     for (int j = 0; j < kPer; ++j) need[j] = (int)threadIdx.x + j * kThreads < n_ent;
@@ -530,8 +586,8 @@ __device__ void gather_rows(const Args& a, int b, int row0, int nrows)
             const int e = (int)threadIdx.x + j * kThreads, r = e / NC, c = e - r * NC;
             const int i = row0 + r;
             const Part* pp = &a.parts[((int64_t)b * (K + 1) + i) * NC + c];
-            const bool ok = i < K ? part_ok<MROW>(pp, ep, r, c, !a.force_recompute)
-                                  : part_ok<MLAST>(pp, ep, r, c, !a.force_recompute);
+            const bool ok = i < K ? part_ok<MROW>(g, pp, ep, r, c, !a.force_recompute)
+                                  : part_ok<MLAST>(g, pp, ep, r, c, !a.force_recompute);
             if (ok && !a.force_recompute)
                 need[j] = false;
             else
@@ -563,9 +619,9 @@ __device__ void gather_rows(const Args& a, int b, int row0, int nrows)
                 const int c = h * 64 + __ffsll((unsigned long long)mk) - 1;
                 mk &= mk - 1;
                 if (i < K)
-                    recompute_part<VEC, MROW, NV>(a, prow, qrow, r, c);
+                    recompute_part<VEC, MROW, NV>(g, a, prow, qrow, r, c);
                 else
-                    recompute_part<VEC, MLAST, NV>(a, prow, qrow, r, c);
+                    recompute_part<VEC, MLAST, NV>(g, a, prow, qrow, r, c);
             }
         }
     }
@@ -579,27 +635,22 @@ struct RowView {
     int arg;
 };
 
-template <int M>
-__device__ __forceinline__ RowView combine_row(int r, int NC)
+template <int M, class G>
+__device__ __forceinline__ RowView combine_row(const G& g, int r, int NC)
 {
     const int lane = threadIdx.x & 63;
     RowView v{0.0, 0.0, 0.0, -INFINITY, INT_MAX};
-    if constexpr ((M & kSP) != 0) v.P = sum_chunks(lds.g.sp[r], NC);
-    if constexpr ((M & kSQ) != 0) v.Q = sum_chunks(lds.g.sq[r], NC);
-    if constexpr ((M & kSMIN) != 0) v.Smin = sum_chunks(lds.g.smin[r], NC);
+    if constexpr ((M & kSP) != 0) v.P = sum_chunks(g.sp[r], NC);
+    if constexpr ((M & kSQ) != 0) v.Q = sum_chunks(g.sq[r], NC);
+    if constexpr ((M & kSMIN) != 0) v.Smin = sum_chunks(g.smin[r], NC);
     if constexpr ((M & kAM) != 0) {
         float mv = -INFINITY;
         int ai = INT_MAX;
         for (int h = 0; h < 2; ++h) {
             const int c = lane + 64 * h;
-            if (c < NC) argmax_merge(mv, ai, am_val(lds.g.am[r][c]), am_arg(lds.g.am[r][c]));
+            if (c < NC) argmax_merge(mv, ai, am_val(g.am[r][c]), am_arg(g.am[r][c]));
         }
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-            const float ov = __shfl_xor(mv, off);
-            const int oi = __shfl_xor(ai, off);
-            argmax_merge(mv, ai, ov, oi);
-        }
+        wave_argmax(mv, ai);
         v.maxv = mv;
         v.arg = ai;
     }
@@ -646,12 +697,13 @@ __device__ __forceinline__ double locate_chunk(const double* m, int NC, double u
 // Search of chunk c for the smallest x with
 // base + sum_{chunk start <= y <= x} w(y) > T, where w is the residual
 // max(0, p*Q - q*P) (RESID) or p itself.  If rounding leaves no such x in
-// the chunk, the last x with w(x) > 0 is taken.  The chunk is re-read with
-// cached loads, one float4 per thread at a time; segment (k, wave) is 256
-// consecutive values and segments are in index order.  All threads of the
-// block must call; the token is returned in every thread.
+// the chunk, the last x with w(x) > 0 is taken.  Each thread loads its whole
+// share of the chunk at once; segment (k, wave) is 256 consecutive values
+// and segments are in index order: the segment masses locate the segment,
+// and the wave that holds it scans its values.  All threads of the block
+// must call; the token is returned in every thread.
 template <bool VEC, bool RESID, int NV>
-__device__ __noinline__ int chunk_draw(Row prow, Row qrow, double P, double Q, int c, double base, double T)
+__device__ __forceinline__ int chunk_draw(Row prow, Row qrow, double P, double Q, int c, double base, double T)
 {
     __shared__ double s_seg[NV][kWaves];
     __shared__ int s_ks, s_ws;
@@ -667,10 +719,15 @@ __device__ __noinline__ int chunk_draw(Row prow, Row qrow, double P, double Q, i
         return t;
     };
 
+    float4 pv[NV], qv[NV];
+#pragma unroll
     for (int k = 0; k < NV; ++k) {
-        const float4 p4 = load_one<VEC, NV>(prow, c, k);
-        const float4 q4 = RESID ? load_one<VEC, NV>(qrow, c, k) : p4;
-        const double s = wave_sum(wsum4(p4, q4));
+        pv[k] = load_one<VEC, NV>(prow, c, k);
+        qv[k] = RESID ? load_one<VEC, NV>(qrow, c, k) : pv[k];
+    }
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+        const double s = wave_sum(wsum4(pv[k], qv[k]));
         if (lane == 0) s_seg[k][w] = s;
     }
     __syncthreads();
@@ -706,8 +763,13 @@ __device__ __noinline__ int chunk_draw(Row prow, Row qrow, double P, double Q, i
     __syncthreads();
     if (w == s_ws) {
         const int k = s_ks;
-        const float4 p4 = load_one<VEC, NV>(prow, c, k);
-        const float4 q4 = RESID ? load_one<VEC, NV>(qrow, c, k) : p4;
+        float4 p4 = pv[0], q4 = qv[0];
+#pragma unroll
+        for (int kk = 1; kk < NV; ++kk)
+            if (kk == k) {
+                p4 = pv[kk];
+                q4 = qv[kk];
+            }
         const double incl = wave_inclusive_scan(wsum4(p4, q4));
         double run = __shfl_up(incl, 1);
         if (lane == 0) run = 0.0;
@@ -755,19 +817,25 @@ __device__ __forceinline__ void write_stats(const Args& a, int64_t row, const Ro
 
 // -------------------------------------------------------- finishing --
 
+// The column whose block finishes sequence b.  Workgroups are handed to the
+// eight XCDs round-robin by index, so a fixed column would put every
+// sequence's finishing work on one XCD; rotating it with b spreads that work
+// over all of them.
+__device__ __forceinline__ int finisher_column(int b, int NC) { return b % NC; }
+
 struct Outcome {
     int n;          // accept-prefix length
     double P, Q;    // masses of row n
     int arg;        // argmax of row n
 };
 
-// Block-cooperative, run by the block of chunk column 0 after its walk:
+// Block-cooperative, run by the finishing block of sequence b after its walk:
 // combine the rows of sequence b in groups of kGroup (wave w takes row
 // g0 + w), take the decisions and, when requested, write the row statistics;
 // without statistics it stops after the group that holds the first
 // rejection.  Uniform result.
-template <bool VEC, bool SAMPLED, int NV, int MROW, int MLAST>
-__device__ Outcome finish_rows(const Args& a, int b)
+template <bool VEC, bool SAMPLED, int NV, int MROW, int MLAST, class G>
+__device__ Outcome finish_rows(G& g, const Args& a, int b)
 {
     __shared__ int s_rej[kGroup], s_arg[kGroup];
     __shared__ double s_P[kGroup], s_Q[kGroup];
@@ -777,12 +845,12 @@ __device__ Outcome finish_rows(const Args& a, int b)
     bool done = false;
     for (int g0 = 0; g0 <= K; g0 += kGroup) {
         const int nrows = (K + 1 - g0) < kGroup ? (K + 1 - g0) : kGroup;
-        gather_rows<VEC, NV, MROW, MLAST>(a, b, g0, nrows);
+        gather_rows<VEC, NV, MROW, MLAST>(g, a, b, g0, nrows);
         if (w < nrows) {
             const int i = g0 + w;
             const int64_t row = (int64_t)b * (K + 1) + i;
             const bool pair = SAMPLED && i < K;
-            const RowView rv = i < K ? combine_row<MROW>(w, NC) : combine_row<MLAST>(w, NC);
+            const RowView rv = i < K ? combine_row<MROW>(g, w, NC) : combine_row<MLAST>(g, w, NC);
             if (lane == 0) {
                 const int tk = i < K ? a.dt[(int64_t)b * K + i] : -1;
                 const bool tin = tk >= 0 && tk < V;
@@ -843,9 +911,9 @@ __global__ __launch_bounds__(kThreads) void sv_greedy_kernel(Args a)
         if (i + 2 <= K) load_chunk<VEC, kVecG>(row_of(tb + (int64_t)(i + 2) * V, V), c, x0);
         publish_part<M>(a, row0 + i + 1, c, block_reduce<M>(thread_stats<M, kVecG>(x1, x1, c)));
     }
-    if (c != 0) return;
+    if (c != finisher_column(b, NC)) return;
 
-    const Outcome o = finish_rows<VEC, false, kVecG, M, M>(a, b);
+    const Outcome o = finish_rows<VEC, false, kVecG, M, M>(lds_greedy, a, b);
     if (threadIdx.x == 0) {
         a.n_out[b] = o.n;
         a.next_out[b] = o.arg;
@@ -1084,13 +1152,13 @@ __global__ __launch_bounds__(kThreads, 4) void sv_sample_kernel(Args a)
         if (pending) decide(K - 1, pl);
         if (state == kSearching) state = K;   // every draft accepted
     }
-    if (c != 0) return;
+    if (c != finisher_column(b, NC)) return;
 
     // finish sequence b: the decisions if this block could not take them
     // (or the row statistics), then the final draw
     int n = state;
     if (STATS || n == kLost) {
-        const Outcome o = finish_rows<VEC, true, kVecS, MP, MB>(a, b);
+        const Outcome o = finish_rows<VEC, true, kVecS, MP, MB>(lds.g, a, b);
         n = o.n;
         Pn = o.P;
         Qn = o.Q;
@@ -1115,9 +1183,9 @@ __global__ __launch_bounds__(kThreads, 4) void sv_sample_kernel(Args a)
         // bonus draw from p_K, or (rounding only) a rejection that left no
         // residual mass: draw from p_n, located by its target chunk masses
         if (n < K)
-            gather_rows<VEC, kVecS, kSP, kSP>(a, b, n, 1);
+            gather_rows<VEC, kVecS, kSP, kSP>(lds.g, a, b, n, 1);
         else
-            gather_rows<VEC, kVecS, kSP, MB>(a, b, n, 1);
+            gather_rows<VEC, kVecS, kSP, MB>(lds.g, a, b, n, 1);
         if (threadIdx.x < 64) {
             int owner;
             double base, T;
