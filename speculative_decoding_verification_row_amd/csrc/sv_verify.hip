@@ -70,6 +70,7 @@ constexpr int kGroup = kWaves;                  // rows the finisher combines at
 static_assert(SV_MAX_V == kMaxNC * kChunkS, "SV_MAX_V must match the chunk geometry");
 constexpr unsigned kEpochs = 255;               // tags 1..255; 0 marks a cleared word
 constexpr double kPollMicroseconds = 200.0;     // bound of a wait before recomputing
+constexpr int kGreedyWalkRows = 1;              // rows a greedy block walks (one: shortest tail)
 
 struct Header {              // 256 bytes
     unsigned error;          // fault word (reserved: nothing in this version sets it)
@@ -115,6 +116,7 @@ struct Args {
     int B, K, V, NC;
     unsigned epoch;                  // this call's tag, 1..255
     int force_recompute;             // test hook: readers recompute every partial
+    int walk_rows;                   // greedy: rows per walk
     unsigned long long poll_ticks;   // wait bound in wall-clock ticks
 };
 
@@ -895,23 +897,27 @@ template <bool VEC, bool STATS>
 __global__ __launch_bounds__(kThreads) void sv_greedy_kernel(Args a)
 {
     constexpr int M = STATS ? (kSP | kAM) : kAM;
-    const int NC = a.NC, K = a.K, V = a.V;
-    const int b = (int)(blockIdx.x / (unsigned)NC);
-    const int c = (int)(blockIdx.x - (unsigned)b * (unsigned)NC);
+    const int NC = a.NC, K = a.K, V = a.V, L = a.walk_rows;
+    const int S = (K + L) / L;                        // walks per column: ceil((K + 1) / L)
+    const unsigned w = blockIdx.x / (unsigned)NC;     // (sequence, segment)
+    const int b = (int)(w / (unsigned)S);
+    const int seg = (int)(w - (unsigned)b * (unsigned)S);
+    const int c = (int)(blockIdx.x - w * (unsigned)NC);
     const float* tb = a.tp + (int64_t)b * (K + 1) * V;
     const int64_t row0 = (int64_t)b * (K + 1);
+    const int r0 = seg * L, r1 = (r0 + L < K + 1) ? r0 + L : K + 1;
 
-    // walk rows 0..K of chunk column c; row i+1 loads while row i reduces
+    // walk rows r0..r1-1 of chunk column c; row i+1 loads while row i reduces
     float4 x0[kVecG], x1[kVecG];
-    load_chunk<VEC, kVecG>(row_of(tb, V), c, x0);
-    for (int i = 0; i <= K; i += 2) {
-        if (i + 1 <= K) load_chunk<VEC, kVecG>(row_of(tb + (int64_t)(i + 1) * V, V), c, x1);
+    load_chunk<VEC, kVecG>(row_of(tb + (int64_t)r0 * V, V), c, x0);
+    for (int i = r0; i < r1; i += 2) {
+        if (i + 1 < r1) load_chunk<VEC, kVecG>(row_of(tb + (int64_t)(i + 1) * V, V), c, x1);
         publish_part<M>(a, row0 + i, c, block_reduce<M>(thread_stats<M, kVecG>(x0, x0, c)));
-        if (i + 1 > K) break;
-        if (i + 2 <= K) load_chunk<VEC, kVecG>(row_of(tb + (int64_t)(i + 2) * V, V), c, x0);
+        if (i + 1 >= r1) break;
+        if (i + 2 < r1) load_chunk<VEC, kVecG>(row_of(tb + (int64_t)(i + 2) * V, V), c, x0);
         publish_part<M>(a, row0 + i + 1, c, block_reduce<M>(thread_stats<M, kVecG>(x1, x1, c)));
     }
-    if (c != finisher_column(b, NC)) return;
+    if (c != finisher_column(b, NC) || seg != S - 1) return;
 
     const Outcome o = finish_rows<VEC, false, kVecG, M, M>(lds_greedy, a, b);
     if (threadIdx.x == 0) {
@@ -1385,7 +1391,9 @@ sv_status sv_verify_greedy_batched(const float* target_probs, const int32_t* dra
     a.force_recompute = tu.force_recompute;
     a.poll_ticks = (unsigned long long)(tu.poll_us * 1e-3 * (double)d.wall_khz);
     const bool vec = (V % 4 == 0) && aligned(target_probs, 16);
-    const dim3 grid((unsigned)((uint64_t)B * (uint64_t)a.NC)), block(kThreads);
+    a.walk_rows = kGreedyWalkRows < K + 1 ? kGreedyWalkRows : K + 1;
+    const uint64_t segs = (uint64_t)(K + a.walk_rows) / (uint64_t)a.walk_rows;
+    const dim3 grid((unsigned)((uint64_t)B * segs * (uint64_t)a.NC)), block(kThreads);
     if (vec && stats)
         hipLaunchKernelGGL((sv_greedy_kernel<true, true>), grid, block, 0, s, a);
     else if (vec)
