@@ -84,7 +84,7 @@ struct Part {                // 32 bytes, one per (row, chunk); tagged words
 };
 
 struct Layout {
-    size_t hdr, parts, wpart, total;
+    size_t hdr, parts, wpart, sstate, total;
 };
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -98,6 +98,7 @@ inline Layout make_layout(int64_t B, int64_t K, int64_t NC, bool sampled)
     L.hdr = o;   o = align_up(o + sizeof(Header), 256);
     L.parts = o; o = align_up(o + (size_t)(B * (K + 1) * NC) * sizeof(Part), 256);
     L.wpart = o; o = align_up(o + (sampled ? (size_t)(B * K * NC) * 8 : 0), 256);
+    L.sstate = o; o = align_up(o + (sampled ? (size_t)B * 8 : 0), 256);
     L.total = o;
     return L;
 }
@@ -113,6 +114,8 @@ struct Args {
     Header* hdr;
     Part* parts;
     unsigned long long* wpart;       // residual chunk masses (sampled)
+    unsigned long long* sstate;      // per-sequence outcome of the walks (sampled)
+    unsigned nwalk;                  // sampled: blocks that walk the draft rows
     int B, K, V, NC;
     unsigned epoch;                  // this call's tag, 1..255
     int force_recompute;             // test hook: readers recompute every partial
@@ -595,7 +598,7 @@ __device__ void gather_rows(G& g, const Args& a, int b, int row0, int nrows)
             else
                 any = true;
         }
-        if (!__syncthreads_or(any)) break;
+        if (!__syncthreads_or(any)) return;   // everything arrived (the usual case)
         if (wait_expired(a, t0)) break;
         __builtin_amdgcn_s_sleep(2);
     }
@@ -733,34 +736,25 @@ __device__ __forceinline__ int chunk_draw(Row prow, Row qrow, double P, double Q
         if (lane == 0) s_seg[k][w] = s;
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
-        double run = base;
-        int ks = -1, ws = 0, lk = 0, lw = 0;
-        double bs = base, lb = base;
-        for (int k = 0; k < NV; ++k) {
-            for (int j = 0; j < kWaves; ++j) {
-                const double s = s_seg[k][j];
-                if (s > 0.0) {
-                    lk = k;
-                    lw = j;
-                    lb = run;
-                }
-                if (ks < 0 && run + s > T) {
-                    ks = k;
-                    ws = j;
-                    bs = run;
-                }
-                run += s;
-            }
+    if (threadIdx.x < 64) {
+        // segment q = k * kWaves + j in lane q: the first segment whose
+        // running mass passes T (or, by rounding only, the last with mass)
+        constexpr int kSegs = NV * kWaves;
+        const int q = threadIdx.x;
+        const double s = q < kSegs ? s_seg[q / kWaves][q % kWaves] : 0.0;
+        const double incl = wave_inclusive_scan(s);
+        double excl = __shfl_up(incl, 1);
+        if (q == 0) excl = 0.0;
+        const double run = base + excl;
+        const unsigned long long mh = __ballot(q < kSegs && run + s > T);
+        const unsigned long long mp = __ballot(q < kSegs && s > 0.0);
+        const int sel = mh ? __ffsll((unsigned long long)mh) - 1 : (mp ? 63 - __clzll(mp) : 0);
+        const double bs = __shfl(run, sel);
+        if (q == 0) {
+            s_ks = sel / kWaves;
+            s_ws = sel % kWaves;
+            s_base = bs;
         }
-        if (ks < 0) {               // rounding: take the last segment with mass
-            ks = lk;
-            ws = lw;
-            bs = lb;
-        }
-        s_ks = ks;
-        s_ws = ws;
-        s_base = bs;
     }
     __syncthreads();
     if (w == s_ws) {
@@ -1056,6 +1050,7 @@ __device__ void gather_resid(const Args& a, int b, int n, double P, double Q, do
         if (wait_expired(a, t0)) break;
         __builtin_amdgcn_s_sleep(2);
     }
+    if (!__syncthreads_or(need || redo)) return;   // everything arrived (the usual case)
     if (threadIdx.x < 2) s_miss[threadIdx.x] = 0ull;
     __syncthreads();
     if (need || redo) atomicOr(&s_miss[c >> 6], 1ull << (c & 63));   // LDS
@@ -1081,94 +1076,19 @@ __device__ void gather_resid(const Args& a, int b, int n, double P, double Q, do
 // since every block takes the same decisions from the same masses).
 enum : int { kSearching = -1, kLost = -2 };
 
-template <bool VEC, bool STATS>
-__global__ __launch_bounds__(kThreads, 4) void sv_sample_kernel(Args a)
+// Block-cooperative: the final draw of sequence b once its accept-prefix
+// length n and the masses of row n are known, and the outputs.  n < K: the
+// inverse CDF of the residual of row n, located by the published residual
+// chunk masses; n == K (or, by rounding only, a rejection that left no
+// residual mass): the inverse CDF of p_n, located by its target chunk masses.
+template <bool VEC, int MB>
+__device__ void draw_and_write(const Args& a, int b, int n, double Pn, double Qn)
 {
-    constexpr int MP = STATS ? (kSP | kSQ | kSMIN | kAM) : (kSP | kSQ);   // rows 0..K-1
-    constexpr int MB = STATS ? (kSP | kAM) : kSP;                        // bonus row K
     __shared__ double s_m[kMaxNC];
     __shared__ int s_owner, s_resid;
     __shared__ double s_base, s_T;
     const int NC = a.NC, K = a.K, V = a.V;
-    const int b = (int)(blockIdx.x / (unsigned)NC);
-    const int c = (int)(blockIdx.x - (unsigned)b * (unsigned)NC);
-    const float* tb = a.tp + (int64_t)b * (K + 1) * V;
-    const float* db = a.dp + (int64_t)b * K * V;
     const int64_t row0 = (int64_t)b * (K + 1);
-
-    // Walk rows 0..K of chunk column c.  At step i row i is in registers
-    // (xp, xq) and row i+1 loads into (yp, yq).  While no draft has been
-    // rejected yet, row i-1 waits in LDS for its decision: its partials were
-    // published by the sibling blocks a step ago and are polled (with the
-    // inputs of its acceptance test) before row i+1's loads are issued, so,
-    // loads returning in order, they arrive while those loads are in flight.
-    // The first rejected row n gets its chunk's residual mass published;
-    // after it the walk only streams and publishes partials.
-    int state = K > 0 ? kSearching : 0;   // kSearching, kLost, or the decided n
-    double Pn = 0.0, Qn = 0.0;
-    int tok = -1;                          // draft token of the pending row (thread 0)
-    float4 xp[kVecS], xq[kVecS], yp[kVecS], yq[kVecS];
-    load_chunk<VEC, kVecS>(row_of(tb, V), c, xp);
-    load_chunk<VEC, kVecS>(row_of(db, K > 0 ? V : 0), c, xq);
-
-    // decide row j (parked) from its poll; publish its residual if rejected
-    auto decide = [&](int j, const Poll& pl) {
-        double P, Q;
-        const int rej = poll_decide(a, b, j, pl, &P, &Q);
-        if (rej < 0) {
-            // masses missing: leave the decision to the finisher, marking the
-            // residuals of every row from j on as "recompute"
-            state = kLost;
-            if (threadIdx.x == 0)
-                for (int r = j; r < K; ++r)
-                    put_u64(&a.wpart[((int64_t)b * K + r) * NC + c], tag_f64(__builtin_nan(""), a.epoch));
-        } else if (rej) {
-            state = j;
-            Pn = P;
-            Qn = Q;
-            const double w = block_sum(parked_resid(P, Q));
-            if (threadIdx.x == 0) put_u64(&a.wpart[((int64_t)b * K + j) * NC + c], tag_f64(w, a.epoch));
-        }
-    };
-
-    for (int i = 0; i < K; ++i) {
-        Poll pl{0ull, 0ull, 0.0f, 0.0f, 0.0f};
-        const bool pending = i > 0 && state == kSearching;
-        if (pending) pl = poll_issue(a, b, i - 1, tok);
-        if (threadIdx.x == 0 && state == kSearching) tok = a.dt[(int64_t)b * K + i];   // row i's token, for step i+1
-        __builtin_amdgcn_sched_barrier(0);
-        const bool next_pair = i + 1 < K;
-        load_chunk<VEC, kVecS>(row_of(tb + (int64_t)(i + 1) * V, V), c, yp);
-        load_chunk<VEC, kVecS>(row_of(db + (next_pair ? (int64_t)(i + 1) * V : 0), next_pair ? V : 0), c, yq);
-        __builtin_amdgcn_sched_barrier(0);
-        publish_part<MP>(a, row0 + i, c, block_reduce<MP>(thread_stats<MP, kVecS>(xp, xq, c)));
-        if (pending) decide(i - 1, pl);
-        if (state == kSearching) park(xp, xq);
-#pragma unroll
-        for (int k = 0; k < kVecS; ++k) {
-            xp[k] = yp[k];
-            xq[k] = yq[k];
-        }
-    }
-    {
-        Poll pl{0ull, 0ull, 0.0f, 0.0f, 0.0f};
-        const bool pending = K > 0 && state == kSearching;
-        if (pending) pl = poll_issue(a, b, K - 1, tok);
-        publish_part<MB>(a, row0 + K, c, block_reduce<MB>(thread_stats<MB, kVecS>(xp, xp, c)));
-        if (pending) decide(K - 1, pl);
-        if (state == kSearching) state = K;   // every draft accepted
-    }
-    if (c != finisher_column(b, NC)) return;
-
-    // finish sequence b: the decisions if this block could not take them
-    // (or the row statistics), then the final draw
-    int n = state;
-    if (STATS || n == kLost) {
-        const Outcome o = finish_rows<VEC, true, kVecS, MP, MB>(lds.g, a, b);
-        n = o.n;
-        Pn = o.P;
-        Qn = o.Q;
-    }
     const double uK = (double)a.u[row0 + K];
     const Row prow = row_of(a.tp + (row0 + n) * V, V);
     const Row qrow = n < K ? row_of(a.dp + ((int64_t)b * K + n) * V, V) : prow;
@@ -1186,8 +1106,6 @@ __global__ __launch_bounds__(kThreads, 4) void sv_sample_kernel(Args a)
     }
     __syncthreads();
     if (!s_resid) {
-        // bonus draw from p_K, or (rounding only) a rejection that left no
-        // residual mass: draw from p_n, located by its target chunk masses
         if (n < K)
             gather_rows<VEC, kVecS, kSP, kSP>(lds.g, a, b, n, 1);
         else
@@ -1212,6 +1130,179 @@ __global__ __launch_bounds__(kThreads, 4) void sv_sample_kernel(Args a)
         a.n_out[b] = n;
         a.next_out[b] = x;
     }
+    __syncthreads();
+}
+
+// The outcome a sequence's finishing walk publishes for the block that
+// finishes its bonus row: n + 1 once n is known (the draw is then already
+// made when n < K), 0 when the walk could not decide; tagged like every
+// published word.
+__device__ __forceinline__ unsigned long long tag_state(int code, unsigned ep)
+{
+    return ((unsigned long long)(unsigned)code << 8) | ep;
+}
+
+// Block-cooperative: the finishing step of sequence b, run by the block of
+// its bonus row that finishes it (the last work of the sequence).
+template <bool VEC, bool STATS>
+__device__ void finish_bonus(const Args& a, int b)
+{
+    constexpr int MP = STATS ? (kSP | kSQ | kSMIN | kAM) : (kSP | kSQ);
+    constexpr int MB = STATS ? (kSP | kAM) : kSP;
+    __shared__ int s_code;
+    const int K = a.K;
+    int n = -1;
+    bool drawn = false;
+    double Pn = 0.0, Qn = 0.0;
+    if (K == 0) {
+        n = 0;
+    } else {
+        // the walks' outcome (published when the walks ended, normally long
+        // before this block runs); without it, decide here from the partials
+        const unsigned long long t0 = wall_clock64();
+        for (;;) {
+            bool got = false;
+            if (threadIdx.x == 0) {
+                const unsigned long long v = get_u64(&a.sstate[b]);
+                got = f64_ok(v, a.epoch) && !a.force_recompute;
+                s_code = got ? (int)(v >> 8) : 0;
+            }
+            if (__syncthreads_or(got)) break;
+            if (wait_expired(a, t0)) break;
+            __builtin_amdgcn_s_sleep(2);
+        }
+        const int code = s_code;
+        __syncthreads();
+        if (code > 0) {
+            n = code - 1;
+            drawn = n < K;
+        }
+    }
+    if (STATS || n < 0) {
+        const Outcome o = finish_rows<VEC, true, kVecS, MP, MB>(lds.g, a, b);
+        n = o.n;
+        Pn = o.P;
+        Qn = o.Q;
+    }
+    if (!drawn) draw_and_write<VEC, MB>(a, b, n, Pn, Qn);
+}
+
+template <bool VEC, bool STATS>
+__global__ __launch_bounds__(kThreads, 4) void sv_sample_kernel(Args a)
+{
+    constexpr int MP = STATS ? (kSP | kSQ | kSMIN | kAM) : (kSP | kSQ);   // rows 0..K-1
+    constexpr int MB = STATS ? (kSP | kAM) : kSP;                        // bonus row K
+    const int NC = a.NC, K = a.K, V = a.V;
+
+    if (blockIdx.x >= a.nwalk) {
+        // Bonus row K (target only), one chunk per block.  These blocks come
+        // after every walk in the grid: they are short, so they keep the
+        // machine busy while the last walks end.  The block of the rotating
+        // finishing column finishes the sequence.
+        const unsigned blk = blockIdx.x - a.nwalk;
+        const int b = (int)(blk / (unsigned)NC);
+        const int c = (int)(blk - (unsigned)b * (unsigned)NC);
+        const int64_t row0 = (int64_t)b * (K + 1);
+        float4 xp[kVecS];
+        load_chunk<VEC, kVecS>(row_of(a.tp + (row0 + K) * V, V), c, xp);
+        publish_part<MB>(a, row0 + K, c, block_reduce<MB>(thread_stats<MB, kVecS>(xp, xp, c)));
+        if (c != finisher_column(b, NC)) return;
+        __builtin_amdgcn_s_setprio(3);   // latency matters here: the last of these end the kernel
+        finish_bonus<VEC, STATS>(a, b);
+        return;
+    }
+
+    // A walk: chunk column c of draft rows 0..K-1 of sequence b (K >= 1).
+    const int b = (int)(blockIdx.x / (unsigned)NC);
+    const int c = (int)(blockIdx.x - (unsigned)b * (unsigned)NC);
+    const float* tb = a.tp + (int64_t)b * (K + 1) * V;
+    const float* db = a.dp + (int64_t)b * K * V;
+    const int64_t row0 = (int64_t)b * (K + 1);
+
+    // At step i row i is in registers (xp, xq) and row i+1 loads into
+    // (yp, yq).  While no draft has been rejected yet, row i-1 waits in LDS
+    // for its decision: its partials were published by the sibling walks a
+    // step ago and are polled (with the inputs of its acceptance test)
+    // before row i+1's loads are issued, so, loads returning in order, they
+    // arrive while those loads are in flight.  The first rejected row n gets
+    // its chunk's residual mass published; after it the walk only streams.
+    int state = kSearching;                // kSearching, kLost, or the decided n
+    double Pn = 0.0, Qn = 0.0;
+    int tok = -1;                          // draft token of the pending row (thread 0)
+    float4 xp[kVecS], xq[kVecS], yp[kVecS], yq[kVecS];
+    load_chunk<VEC, kVecS>(row_of(tb, V), c, xp);
+    load_chunk<VEC, kVecS>(row_of(db, V), c, xq);
+
+    // decide row j (parked) from its poll; publish its residual if rejected
+    auto decide = [&](int j, const Poll& pl) {
+        double P, Q;
+        const int rej = poll_decide(a, b, j, pl, &P, &Q);
+        if (rej < 0) {
+            // masses missing: leave the decision to the finisher, marking the
+            // residuals of every row from j on as "recompute"
+            state = kLost;
+            if (threadIdx.x == 0)
+                for (int r = j; r < K; ++r)
+                    put_u64(&a.wpart[((int64_t)b * K + r) * NC + c], tag_f64(__builtin_nan(""), a.epoch));
+        } else if (rej) {
+            state = j;
+            Pn = P;
+            Qn = Q;
+            const double w = block_sum(parked_resid(P, Q));
+            if (threadIdx.x == 0) put_u64(&a.wpart[((int64_t)b * K + j) * NC + c], tag_f64(w, a.epoch));
+        }
+    };
+    // row i+1's loads (an empty range after the last draft row reads zeros)
+    auto load_next = [&](int i) {
+        const bool more = i + 1 < K;
+        const int64_t off = more ? (int64_t)(i + 1) * V : 0;
+        load_chunk<VEC, kVecS>(row_of(tb + off, more ? V : 0), c, yp);
+        load_chunk<VEC, kVecS>(row_of(db + off, more ? V : 0), c, yq);
+    };
+
+    int i = 0;
+    for (; i < K; ++i) {   // searching: decisions one step behind, rows parked
+        Poll pl{0ull, 0ull, 0.0f, 0.0f, 0.0f};
+        const bool pending = i > 0;
+        if (pending) pl = poll_issue(a, b, i - 1, tok);
+        if (threadIdx.x == 0) tok = a.dt[(int64_t)b * K + i];   // row i's token, for step i+1
+        __builtin_amdgcn_sched_barrier(0);
+        load_next(i);
+        __builtin_amdgcn_sched_barrier(0);
+        publish_part<MP>(a, row0 + i, c, block_reduce<MP>(thread_stats<MP, kVecS>(xp, xq, c)));
+        if (pending) decide(i - 1, pl);
+        if (state == kSearching) park(xp, xq);
+#pragma unroll
+        for (int k = 0; k < kVecS; ++k) {
+            xp[k] = yp[k];
+            xq[k] = yq[k];
+        }
+        if (state != kSearching) {
+            ++i;
+            break;
+        }
+    }
+    for (; i < K; ++i) {   // after the first rejection (or a lost decision)
+        load_next(i);
+        __builtin_amdgcn_sched_barrier(0);
+        publish_part<MP>(a, row0 + i, c, block_reduce<MP>(thread_stats<MP, kVecS>(xp, xq, c)));
+#pragma unroll
+        for (int k = 0; k < kVecS; ++k) {
+            xp[k] = yp[k];
+            xq[k] = yq[k];
+        }
+    }
+    if (state == kSearching) {   // the last draft row's decision
+        decide(K - 1, poll_issue(a, b, K - 1, tok));
+        if (state == kSearching) state = K;   // every draft accepted
+    }
+    if (c != finisher_column(b, NC)) return;
+
+    // The finishing walk of sequence b draws when a draft was rejected and
+    // publishes the outcome for the block that finishes the bonus row.
+    __builtin_amdgcn_s_setprio(3);
+    if (state >= 0 && state < K) draw_and_write<VEC, MB>(a, b, state, Pn, Qn);
+    if (threadIdx.x == 0) put_u64(&a.sstate[b], tag_state(state >= 0 ? state + 1 : 0, a.epoch));
 }
 
 __global__ void sv_fill_zero_kernel(uint4* p, size_t n16)
@@ -1328,6 +1419,7 @@ Args make_args(void* ws, int32_t B, int32_t K, int32_t V, bool sampled)
     a.hdr = reinterpret_cast<Header*>(w + L.hdr);
     a.parts = reinterpret_cast<Part*>(w + L.parts);
     a.wpart = reinterpret_cast<unsigned long long*>(w + L.wpart);
+    a.sstate = reinterpret_cast<unsigned long long*>(w + L.sstate);
     a.B = B;
     a.K = K;
     a.V = V;
@@ -1442,7 +1534,9 @@ sv_status sv_verify_sample_batched(const float* target_probs, const float* draft
     a.force_recompute = tu.force_recompute;
     a.poll_ticks = (unsigned long long)(tu.poll_us * 1e-3 * (double)d.wall_khz);
     const bool vec = (V % 4 == 0) && aligned(target_probs, 16) && (K == 0 || aligned(draft_probs, 16));
-    const dim3 grid((unsigned)((uint64_t)B * (uint64_t)a.NC)), block(kThreads);
+    const uint64_t per_row = (uint64_t)B * (uint64_t)a.NC;
+    a.nwalk = (unsigned)(K > 0 ? per_row : 0);   // the walks, then the bonus-row blocks
+    const dim3 grid((unsigned)(a.nwalk + per_row)), block(kThreads);
     if (vec && stats)
         hipLaunchKernelGGL((sv_sample_kernel<true, true>), grid, block, 0, s, a);
     else if (vec)
