@@ -70,6 +70,7 @@ constexpr int kGroup = kWaves;                  // rows the finisher combines at
 static_assert(SV_MAX_V == kMaxNC * kChunkS, "SV_MAX_V must match the chunk geometry");
 constexpr unsigned kEpochs = 255;               // tags 1..255; 0 marks a cleared word
 constexpr double kPollMicroseconds = 200.0;     // bound of a wait before recomputing
+constexpr int kBonusChunks = 2;                 // bonus-row chunks per block (sampled)
 constexpr int kGreedyWalkRows = 1;              // rows a greedy block walks (one: shortest tail)
 
 struct Header {              // 256 bytes
@@ -1199,14 +1200,22 @@ __global__ __launch_bounds__(kThreads, 4) void sv_sample_kernel(Args a)
         // after every walk in the grid: they are short, so they keep the
         // machine busy while the last walks end.  The block of the rotating
         // finishing column finishes the sequence.
+        const int per_seq = (NC + kBonusChunks - 1) / kBonusChunks;
         const unsigned blk = blockIdx.x - a.nwalk;
-        const int b = (int)(blk / (unsigned)NC);
-        const int c = (int)(blk - (unsigned)b * (unsigned)NC);
+        const int b = (int)(blk / (unsigned)per_seq);
+        const int c0 = (int)(blk - (unsigned)b * (unsigned)per_seq) * kBonusChunks;
         const int64_t row0 = (int64_t)b * (K + 1);
-        float4 xp[kVecS];
-        load_chunk<VEC, kVecS>(row_of(a.tp + (row0 + K) * V, V), c, xp);
-        publish_part<MB>(a, row0 + K, c, block_reduce<MB>(thread_stats<MB, kVecS>(xp, xp, c)));
-        if (c != finisher_column(b, NC)) return;
+        const Row prow = row_of(a.tp + (row0 + K) * V, V);
+        float4 xp[kBonusChunks][kVecS];
+#pragma unroll
+        for (int j = 0; j < kBonusChunks; ++j)   // chunks past NC read as zeros
+            load_chunk<VEC, kVecS>(prow, c0 + j < NC ? c0 + j : NC, xp[j]);
+#pragma unroll
+        for (int j = 0; j < kBonusChunks; ++j)
+            if (c0 + j < NC)
+                publish_part<MB>(a, row0 + K, c0 + j, block_reduce<MB>(thread_stats<MB, kVecS>(xp[j], xp[j], c0 + j)));
+        const int fc = finisher_column(b, NC);
+        if (fc < c0 || fc >= c0 + kBonusChunks) return;
         __builtin_amdgcn_s_setprio(3);   // latency matters here: the last of these end the kernel
         finish_bonus<VEC, STATS>(a, b);
         return;
@@ -1535,8 +1544,9 @@ sv_status sv_verify_sample_batched(const float* target_probs, const float* draft
     a.poll_ticks = (unsigned long long)(tu.poll_us * 1e-3 * (double)d.wall_khz);
     const bool vec = (V % 4 == 0) && aligned(target_probs, 16) && (K == 0 || aligned(draft_probs, 16));
     const uint64_t per_row = (uint64_t)B * (uint64_t)a.NC;
+    const uint64_t bonus = (uint64_t)B * (uint64_t)((a.NC + kBonusChunks - 1) / kBonusChunks);
     a.nwalk = (unsigned)(K > 0 ? per_row : 0);   // the walks, then the bonus-row blocks
-    const dim3 grid((unsigned)(a.nwalk + per_row)), block(kThreads);
+    const dim3 grid((unsigned)(a.nwalk + bonus)), block(kThreads);
     if (vec && stats)
         hipLaunchKernelGGL((sv_sample_kernel<true, true>), grid, block, 0, s, a);
     else if (vec)
