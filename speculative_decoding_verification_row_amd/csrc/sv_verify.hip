@@ -71,6 +71,7 @@ static_assert(SV_MAX_V == kMaxNC * kChunkS, "SV_MAX_V must match the chunk geome
 constexpr unsigned kEpochs = 255;               // tags 1..255; 0 marks a cleared word
 constexpr double kPollMicroseconds = 200.0;     // bound of a wait before recomputing
 constexpr int kBonusChunks = 2;                 // bonus-row chunks per block (sampled)
+constexpr unsigned kTailBlocks = 2048;          // the last two waves of 256 CUs x 4 resident blocks
 constexpr int kGreedyWalkRows = 1;              // rows a greedy block walks (one: shortest tail)
 
 struct Header {              // 256 bytes
@@ -207,23 +208,34 @@ __device__ __forceinline__ float4 as_float4(u32x4 v)
 // Streaming loads of float4 numbers k in [0, NV) of chunk c; all of a
 // thread's loads are issued back to back and stay in flight together.  The
 // scalar form (rows not 16-byte aligned, or V not a multiple of 4) reads
-// the same values one float at a time.
-template <bool VEC, int NV>
+// the same values one float at a time.  AUX is the cache policy.
+template <bool VEC, int NV, int AUX = kNonTemporal>
 __device__ __forceinline__ void load_chunk(Row row, int c, float4 (&v)[NV])
 {
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
         const int off = f4_index<NV>(c, k) * 16;
         if constexpr (VEC) {
-            v[k] = as_float4(__builtin_amdgcn_raw_buffer_load_b128(row.r, off, 0, kNonTemporal));
+            v[k] = as_float4(__builtin_amdgcn_raw_buffer_load_b128(row.r, off, 0, AUX));
         } else {
             float e[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                e[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(row.r, off + 4 * j, 0, kNonTemporal));
+                e[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(row.r, off + 4 * j, 0, AUX));
             v[k] = make_float4(e[0], e[1], e[2], e[3]);
         }
     }
+}
+
+// The same loads, kept in the caches when `keep`: for the last blocks of the
+// grid, whose chunks a finishing block may read again soon after.
+template <bool VEC, int NV>
+__device__ __forceinline__ void load_chunk_keep(Row row, int c, float4 (&v)[NV], bool keep)
+{
+    if (keep)
+        load_chunk<VEC, NV, 0>(row, c, v);
+    else
+        load_chunk<VEC, NV>(row, c, v);
 }
 
 // Cached load of float4 number k (runtime) of chunk c.
@@ -1209,7 +1221,7 @@ __global__ __launch_bounds__(kThreads, 4) void sv_sample_kernel(Args a)
         float4 xp[kBonusChunks][kVecS];
 #pragma unroll
         for (int j = 0; j < kBonusChunks; ++j)   // chunks past NC read as zeros
-            load_chunk<VEC, kVecS>(prow, c0 + j < NC ? c0 + j : NC, xp[j]);
+            load_chunk_keep<VEC, kVecS>(prow, c0 + j < NC ? c0 + j : NC, xp[j], blk + kTailBlocks >= gridDim.x - a.nwalk);
 #pragma unroll
         for (int j = 0; j < kBonusChunks; ++j)
             if (c0 + j < NC)
