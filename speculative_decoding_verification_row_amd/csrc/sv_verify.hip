@@ -7,28 +7,32 @@
 // silent are stated in include/sv_verify.h.
 //
 // Work decomposition (the vocabulary axis is the long one):
-//   * every row of V values is cut into NC chunks (4096 values in sampled
-//     mode, 8192 in greedy mode).  One 256-thread block (4 waves) owns chunk
-//     column c of sequence b and walks the rows of b in order: target row 0
-//     with draft row 0, row 1, ..., and last the bonus row K (target only).
-//     Each thread issues coalesced, non-temporal 16-byte loads, and the next
-//     row's chunk is loaded while the current one is reduced, so a block
-//     keeps loads in flight.  The grid is B * NC blocks, one per (b, c).
-//   * per-chunk partials (fp64 masses of p, q and min(p, q); lowest-index
-//     argmax) are published to the workspace as tagged words (below).
-//   * sampled mode: once row i+1 is loading, the block gathers the partials
-//     of row i from the NC sibling blocks of sequence b (they walk the same
-//     rows at the same time), forms the row masses P_i and Q_i, and publishes
-//     its chunk's residual mass sum max(0, p*Q - q*P) from the row-i data it
-//     still holds in registers.  No row is read twice: the final draw
-//     re-reads a single chunk.
-//   * one block of each sequence (its column rotates with b, so that the
-//     work spreads over the XCDs) finishes the sequence after its walk: it
-//     combines the rows (in chunk order), takes the acceptance decisions and
-//     the accept-prefix length n, and emits the next token -- argmax of row n
-//     (greedy), or an inverse-CDF draw over the residual of row n or over
-//     the bonus row (sampled), whose chunk is located from the published
-//     chunk masses and then searched.
+//   * every row of V values is cut into NC chunks: 4096 values in sampled
+//     mode, 8192 in greedy mode.  A block has 256 threads (4 waves); each
+//     thread issues coalesced 16-byte loads, all of a chunk's loads in flight
+//     together, non-temporal except in the last blocks of the sampled grid
+//     (a finishing block may read their chunks again soon after).
+//   * greedy: one block per (row, chunk), B * (K+1) * NC blocks.  Each
+//     publishes its chunk's (max, lowest-index argmax); the block of row K in
+//     a column that rotates with b combines the rows of sequence b in chunk
+//     order, takes the decisions, and writes n and the argmax of row n.
+//   * sampled: one walk block per (sequence b, chunk column c) streams target
+//     and draft rows 0..K-1 of its column, the next row loading while the
+//     current one is reduced, and publishes per row its chunk's fp64 masses
+//     of p and q.  The acceptance test of row i needs the row masses P_i and
+//     Q_i, so the partials of all NC sibling walks, which stream the same
+//     rows at the same time: a walk decides row i one step later, polling
+//     its partials just before it issues row i+2's loads (loads return in
+//     order, so they arrive first), and keeps row i parked in LDS meanwhile.
+//     At the first rejected row n every walk publishes its chunk's residual
+//     mass sum max(0, p*Q - q*P) from the parked row, then only streams.  The
+//     walk of a column that rotates with b draws from the residual of row n
+//     (the chunk is located from the published residual masses, then
+//     searched) and publishes the sequence's outcome.  The bonus row K is
+//     read by short blocks at the end of the grid (two chunks each), which
+//     keep the machine busy while the last walks end; the one of the
+//     rotating column finishes the sequence, drawing the bonus token from
+//     p_K after full acceptance.
 //   * every result depends on V alone (fixed chunking and combine order),
 //     never on B, K, the launch shape or timing.
 //

@@ -40,18 +40,24 @@ def _to_dev(*arrays):
     return [None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(DEV) for a in arrays]
 
 
-def run_greedy(tp, dt, **kw):
+def _outs(r, stats):
+    """numpy outputs of a verify call; stats None when none were requested."""
+    torch.cuda.synchronize()
+    if stats:
+        n, nx, st = r
+        return n.cpu().numpy(), nx.cpu().numpy(), sv.stats_to_numpy(st)
+    n, nx = r
+    return n.cpu().numpy(), nx.cpu().numpy(), None
+
+
+def run_greedy(tp, dt, stats=True, **kw):
     tpd, dtd = _to_dev(tp, dt)
-    n, nx, st = sv.sv_verify_greedy_batched(tpd, dtd, stats=True, **kw)
-    torch.cuda.synchronize()
-    return n.cpu().numpy(), nx.cpu().numpy(), sv.stats_to_numpy(st)
+    return _outs(sv.sv_verify_greedy_batched(tpd, dtd, stats=stats or None, **kw), stats)
 
 
-def run_sample(tp, dp, dt, u, **kw):
+def run_sample(tp, dp, dt, u, stats=True, **kw):
     tpd, dpd, dtd, ud = _to_dev(tp, dp, dt, u)
-    n, nx, st = sv.sv_verify_sample_batched(tpd, dpd, dtd, ud, stats=True, **kw)
-    torch.cuda.synchronize()
-    return n.cpu().numpy(), nx.cpu().numpy(), sv.stats_to_numpy(st)
+    return _outs(sv.sv_verify_sample_batched(tpd, dpd, dtd, ud, stats=stats or None, **kw), stats)
 
 
 def _random_rows(rng, B, K, V, ties=True, zeros=True):
@@ -82,44 +88,51 @@ SMALL = [(1, 0, 1), (3, 0, 7), (2, 1, 2), (4, 2, 3), (5, 4, 1000), (3, 3, 1003),
          (2, 3, 8193), (2, 2, 16389), (3, 4, 32000), (2, 5, 40001), (1, 2, 65536 + 4)]
 
 
+# Both kernel variants: with row statistics, and without (the configuration
+# the benchmark times, whose finishing work differs).
+STATS = [True, False]
+
+
+@pytest.mark.parametrize("stats", STATS, ids=["stats", "nostats"])
 @pytest.mark.parametrize("B,K,V", SMALL, ids=lambda x: str(x))
-def test_greedy_small(B, K, V):
-    _case(f"greedy small B={B} K={K} V={V}")
+def test_greedy_small(B, K, V, stats):
+    _case(f"greedy small B={B} K={K} V={V} stats={stats}")
     rng = np.random.default_rng(B * 1000 + K * 100 + V)
     p, _, t, _ = _random_rows(rng, B, K, V)
-    n, nx, st = run_greedy(p, t)
+    n, nx, st = run_greedy(p, t, stats=stats)
     check_greedy(n, nx, st, oracle.verify_greedy(p, t))
 
 
+@pytest.mark.parametrize("stats", STATS, ids=["stats", "nostats"])
 @pytest.mark.parametrize("B,K,V", SMALL, ids=lambda x: str(x))
-def test_sampled_small(B, K, V):
-    _case(f"sampled small B={B} K={K} V={V}")
+def test_sampled_small(B, K, V, stats):
+    _case(f"sampled small B={B} K={K} V={V} stats={stats}")
     rng = np.random.default_rng(7 + B * 1000 + K * 100 + V)
     p, q, t, u = _random_rows(rng, B, K, V)
-    n, nx, st = run_sample(p, q, t, u)
+    n, nx, st = run_sample(p, q, t, u, stats=stats)
     check_sampled(n, nx, st, oracle.verify_sample(p, q, t, u))
 
 
+@pytest.mark.parametrize("stats", STATS, ids=["stats", "nostats"])
 @pytest.mark.parametrize("family,B,K,V", [("c1", 16, 4, 32000), ("c3", 24, 5, 24577),
                                           ("c4", 32, 8, 12000), ("c5", 6, 16, 30011)])
-def test_sampled_families_reduced(family, B, K, V):
-    _case(f"sampled {family} B={B} K={K} V={V}")
+def test_sampled_families_reduced(family, B, K, V, stats):
+    _case(f"sampled {family} B={B} K={K} V={V} stats={stats}")
     b = workloads.make_batch(family, B, K, V, seed=5)
     args = (b.target_probs, b.draft_probs, b.draft_tokens, b.uniforms)
-    n, nx, st = run_sample(*args)
+    n, nx, st = run_sample(*args, stats=stats)
     rep = check_sampled(n, nx, st, oracle.verify_sample(*args))
     print(f"  parity {rep}")
 
 
 # ------------------------------------------------------------ workloads --
 
-def _gpu_outputs(db, sampled):
+def _gpu_outputs(db, sampled, stats=True):
     if sampled:
-        n, nx, st = sv.sv_verify_sample_batched(db["tp"], db["dp"], db["dt"], db["u"], stats=True)
+        r = sv.sv_verify_sample_batched(db["tp"], db["dp"], db["dt"], db["u"], stats=stats or None)
     else:
-        n, nx, st = sv.sv_verify_greedy_batched(db["tp"], db["dt"], stats=True)
-    torch.cuda.synchronize()
-    return n.cpu().numpy(), nx.cpu().numpy(), sv.stats_to_numpy(st)
+        r = sv.sv_verify_greedy_batched(db["tp"], db["dt"], stats=stats or None)
+    return _outs(r, stats)
 
 
 def _oracle_on(c, rows, sampled, seed=0):
@@ -137,16 +150,20 @@ def test_workload_full_size(cfg, mode):
     sampled = mode == "sampled"
     _case(f"workload {cfg} {mode} B={c['B']} K={c['K']} V={c['V']} (generating)")
     db = device_batch(c["family"], c["B"], c["K"], c["V"], seed=0, device=DEV, sampled=sampled)
-    _case(f"workload {cfg} {mode}: running")
+    _case(f"workload {cfg} {mode}: running, with row statistics and without (the benchmark's launch)")
     n, nx, st = _gpu_outputs(db, sampled)
+    n0, nx0, _ = _gpu_outputs(db, sampled, stats=False)
     B, K, V = c["B"], c["K"], c["V"]
     assert np.all((n >= 0) & (n <= K)) and np.all((nx >= 0) & (nx < V))
+    # both variants take every decision from the same words: identical outputs
+    assert np.array_equal(n0, n) and np.array_equal(nx0, nx)
     rows = None
     if B > 256:
         rows = np.sort(np.random.default_rng(cfg).choice(B, size=128, replace=False))
     orc, hb = _oracle_on(c, rows, sampled)
     if sampled:
         rep = check_sampled(n, nx, st, orc, rows=rows)
+        check_sampled(n0, nx0, None, orc, rows=rows)
         print(f"  parity {rep}")
         if cfg == 4:
             qeqp = np.array([d["q_equals_p"] for d in db["info"]])
@@ -154,6 +171,7 @@ def test_workload_full_size(cfg, mode):
             assert np.all(n[qeqp] == K)            # q = p accepts every draft
     else:
         check_greedy(n, nx, st, orc, rows=rows)
+        check_greedy(n0, nx0, None, orc, rows=rows)
         if cfg == 2:
             m = np.array([d["m"] for d in db["info"]])
             assert np.array_equal(n, m)
@@ -276,11 +294,10 @@ def test_edge_unaligned_rows_use_scalar_path():
     tpd.copy_(torch.from_numpy(p))
     dpd.copy_(torch.from_numpy(q))
     dtd, ud = _to_dev(t, u)
-    n, nx, st = sv.sv_verify_sample_batched(tpd, dpd, dtd, ud, stats=True)
-    check_sampled(n.cpu().numpy(), nx.cpu().numpy(), sv.stats_to_numpy(st),
-                  oracle.verify_sample(p, q, t, u))
-    n, nx, st = sv.sv_verify_greedy_batched(tpd, dtd, stats=True)
-    check_greedy(n.cpu().numpy(), nx.cpu().numpy(), sv.stats_to_numpy(st), oracle.verify_greedy(p, t))
+    os_, og = oracle.verify_sample(p, q, t, u), oracle.verify_greedy(p, t)
+    for stats in STATS:
+        check_sampled(*_outs(sv.sv_verify_sample_batched(tpd, dpd, dtd, ud, stats=stats or None), stats), os_)
+        check_greedy(*_outs(sv.sv_verify_greedy_batched(tpd, dtd, stats=stats or None), stats), og)
 
 
 # ------------------------------------------ determinism and B-invariance --
