@@ -952,7 +952,7 @@ __device__ __forceinline__ Poll poll_issue(const Args& a, int b, int i, int tok)
     Poll p{0ull, 0ull, 0.0f, 0.0f, 0.0f};
     const int t = threadIdx.x, K = a.K, V = a.V;
     const int64_t row = (int64_t)b * (K + 1) + i;
-    if (t < a.NC) {
+    if (t < a.NC && t < 64) {   // chunk t in lane t of wave 0 (poll_decide polls t + 64)
         const Part* pp = a.parts + row * a.NC + t;
         p.sp = get_u64(&pp->sp);
         p.sq = get_u64(&pp->sq);
@@ -972,47 +972,64 @@ __device__ __forceinline__ Poll poll_issue(const Args& a, int b, int i, int tok)
 // when some partial is still missing at the wait bound.  Uniform result.
 __device__ int poll_decide(const Args& a, int b, int i, Poll pl, double* P, double* Q)
 {
-    __shared__ double s_sp[kMaxNC], s_sq[kMaxNC], s_PQ[2];
+    __shared__ double s_PQ[2];
     __shared__ int s_rej;
     const int NC = a.NC, t = threadIdx.x;
     const unsigned ep = a.epoch;
     const int64_t row = (int64_t)b * (a.K + 1) + i;
-    bool need = t < NC;
-    const unsigned long long t0 = wall_clock64();
-    for (;;) {
-        bool any = false;
-        if (need) {
-            if (f64_ok(pl.sp, ep) && f64_ok(pl.sq, ep) && !a.force_recompute) {
-                s_sp[t] = f64_of(pl.sp);
-                s_sq[t] = f64_of(pl.sq);
-                need = false;
-            } else {
-                any = true;
+    // Wave 0 decides alone: lane t holds chunks t (polled by poll_issue) and
+    // t + 64 (polled here, rows of more than 64 chunks only); tags are
+    // checked by ballot and the sums are those of sum_chunks, in registers.
+    // One barrier then hands the result to the block.
+    if (t < 64) {
+        const Part* p0 = a.parts + row * NC + t;
+        const Part* p1 = p0 + 64;
+        bool need0 = t < NC, need1 = t + 64 < NC;
+        unsigned long long w1p = 0ull, w1q = 0ull;
+        if (need1) {
+            w1p = get_u64(&p1->sp);
+            w1q = get_u64(&p1->sq);
+        }
+        double s0p = 0.0, s0q = 0.0, s1p = 0.0, s1q = 0.0;
+        const unsigned long long t0 = wall_clock64();
+        for (;;) {
+            if (need0 && f64_ok(pl.sp, ep) && f64_ok(pl.sq, ep) && !a.force_recompute) {
+                s0p = f64_of(pl.sp);
+                s0q = f64_of(pl.sq);
+                need0 = false;
+            }
+            if (need1 && f64_ok(w1p, ep) && f64_ok(w1q, ep) && !a.force_recompute) {
+                s1p = f64_of(w1p);
+                s1q = f64_of(w1q);
+                need1 = false;
+            }
+            if (__ballot(need0 || need1) == 0ull) break;
+            if (a.force_recompute || wall_clock64() - t0 > a.poll_ticks) break;
+            __builtin_amdgcn_s_sleep(2);
+            if (need0) {
+                pl.sp = get_u64(&p0->sp);
+                pl.sq = get_u64(&p0->sq);
+            }
+            if (need1) {
+                w1p = get_u64(&p1->sp);
+                w1q = get_u64(&p1->sq);
             }
         }
-        if (!__syncthreads_or(any)) break;
-        if (wait_expired(a, t0)) return -1;
-        __builtin_amdgcn_s_sleep(2);
-        if (need) {
-            const Part* pp = a.parts + row * NC + t;
-            pl.sp = get_u64(&pp->sp);
-            pl.sq = get_u64(&pp->sq);
-        }
-    }
-    if (t < 64) {
-        const double p = sum_chunks(s_sp, NC), q = sum_chunks(s_sq, NC);
-        if (t == 0) {
-            s_PQ[0] = p;
-            s_PQ[1] = q;
-            s_rej = accepted(pl.u, pl.pt, pl.qt, p, q) ? 0 : 1;
+        if (__ballot(need0 || need1) == 0ull) {
+            const double p = wave_sum(s0p + s1p), q = wave_sum(s0q + s1q);
+            if (t == 0) {
+                s_PQ[0] = p;
+                s_PQ[1] = q;
+                s_rej = accepted(pl.u, pl.pt, pl.qt, p, q) ? 0 : 1;
+            }
+        } else if (t == 0) {
+            s_rej = -1;
         }
     }
     __syncthreads();
     *P = s_PQ[0];
     *Q = s_PQ[1];
-    const int rej = s_rej;
-    __syncthreads();
-    return rej;
+    return s_rej;
 }
 
 // Park this thread's share of a row chunk in LDS, and the residual sum of
