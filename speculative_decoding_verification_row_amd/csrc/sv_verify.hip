@@ -448,37 +448,40 @@ __device__ __forceinline__ double wave_inclusive_scan(double v)
 }
 
 // Block reduction of the fields in M; the result is valid in thread 0.
-// Ends with a barrier, so the block may call it again at once.
-template <int M>
-__device__ __forceinline__ Acc block_reduce(Acc a)
+// With TRAIL it ends with a barrier, so the block may call it again at once.
+// Without, the caller alternates `slot` between consecutive calls: a slot is
+// written again only two calls later, after every wave, thread 0 included
+// (which has read it by then), has passed the barrier of the call between.
+template <int M, bool TRAIL = true>
+__device__ __forceinline__ Acc block_reduce(Acc a, int slot = 0)
 {
-    __shared__ double s_sp[kWaves], s_sq[kWaves], s_sm[kWaves];
-    __shared__ float s_v[kWaves];
-    __shared__ int s_i[kWaves];
+    __shared__ double s_sp[2][kWaves], s_sq[2][kWaves], s_sm[2][kWaves];
+    __shared__ float s_v[2][kWaves];
+    __shared__ int s_i[2][kWaves];
     if constexpr ((M & kSP) != 0) a.sp = wave_sum(a.sp);
     if constexpr ((M & kSQ) != 0) a.sq = wave_sum(a.sq);
     if constexpr ((M & kSMIN) != 0) a.smin = wave_sum(a.smin);
     if constexpr ((M & kAM) != 0) wave_argmax(a.maxv, a.arg);
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     if (lane == 0) {
-        s_sp[w] = a.sp;
-        s_sq[w] = a.sq;
-        s_sm[w] = a.smin;
-        s_v[w] = a.maxv;
-        s_i[w] = a.arg;
+        s_sp[slot][w] = a.sp;
+        s_sq[slot][w] = a.sq;
+        s_sm[slot][w] = a.smin;
+        s_v[slot][w] = a.maxv;
+        s_i[slot][w] = a.arg;
     }
     __syncthreads();
     Acc r = a;
     if (threadIdx.x == 0) {
-        r = Acc{s_sp[0], s_sq[0], s_sm[0], s_v[0], s_i[0]};
+        r = Acc{s_sp[slot][0], s_sq[slot][0], s_sm[slot][0], s_v[slot][0], s_i[slot][0]};
         for (int j = 1; j < kWaves; ++j) {
-            r.sp += s_sp[j];
-            r.sq += s_sq[j];
-            r.smin += s_sm[j];
-            argmax_merge(r.maxv, r.arg, s_v[j], s_i[j]);
+            r.sp += s_sp[slot][j];
+            r.sq += s_sq[slot][j];
+            r.smin += s_sm[slot][j];
+            argmax_merge(r.maxv, r.arg, s_v[slot][j], s_i[slot][j]);
         }
     }
-    __syncthreads();
+    if (TRAIL) __syncthreads();
     return r;
 }
 
@@ -923,10 +926,10 @@ __global__ __launch_bounds__(kThreads) void sv_greedy_kernel(Args a)
     load_chunk<VEC, kVecG>(row_of(tb + (int64_t)r0 * V, V), c, x0);
     for (int i = r0; i < r1; i += 2) {
         if (i + 1 < r1) load_chunk<VEC, kVecG>(row_of(tb + (int64_t)(i + 1) * V, V), c, x1);
-        publish_part<M>(a, row0 + i, c, block_reduce<M>(thread_stats<M, kVecG>(x0, x0, c)));
+        publish_part<M>(a, row0 + i, c, block_reduce<M, false>(thread_stats<M, kVecG>(x0, x0, c), 0));
         if (i + 1 >= r1) break;
         if (i + 2 < r1) load_chunk<VEC, kVecG>(row_of(tb + (int64_t)(i + 2) * V, V), c, x0);
-        publish_part<M>(a, row0 + i + 1, c, block_reduce<M>(thread_stats<M, kVecG>(x1, x1, c)));
+        publish_part<M>(a, row0 + i + 1, c, block_reduce<M, false>(thread_stats<M, kVecG>(x1, x1, c), 1));
     }
     if (c != finisher_column(b, NC) || seg != S - 1) return;
 
@@ -1246,7 +1249,7 @@ __global__ __launch_bounds__(kThreads, 4) void sv_sample_kernel(Args a)
 #pragma unroll
         for (int j = 0; j < kBonusChunks; ++j)
             if (c0 + j < NC)
-                publish_part<MB>(a, row0 + K, c0 + j, block_reduce<MB>(thread_stats<MB, kVecS>(xp[j], xp[j], c0 + j)));
+                publish_part<MB>(a, row0 + K, c0 + j, block_reduce<MB, false>(thread_stats<MB, kVecS>(xp[j], xp[j], c0 + j), j & 1));
         const int fc = finisher_column(b, NC);
         if (fc < c0 || fc >= c0 + kBonusChunks) return;
         __builtin_amdgcn_s_setprio(3);   // latency matters here: the last of these end the kernel
@@ -1311,7 +1314,7 @@ __global__ __launch_bounds__(kThreads, 4) void sv_sample_kernel(Args a)
         __builtin_amdgcn_sched_barrier(0);
         load_next(i);
         __builtin_amdgcn_sched_barrier(0);
-        publish_part<MP>(a, row0 + i, c, block_reduce<MP>(thread_stats<MP, kVecS>(xp, xq, c)));
+        publish_part<MP>(a, row0 + i, c, block_reduce<MP, false>(thread_stats<MP, kVecS>(xp, xq, c), i & 1));
         if (pending) decide(i - 1, pl);
         if (state == kSearching) park(xp, xq);
 #pragma unroll
@@ -1327,7 +1330,7 @@ __global__ __launch_bounds__(kThreads, 4) void sv_sample_kernel(Args a)
     for (; i < K; ++i) {   // after the first rejection (or a lost decision)
         load_next(i);
         __builtin_amdgcn_sched_barrier(0);
-        publish_part<MP>(a, row0 + i, c, block_reduce<MP>(thread_stats<MP, kVecS>(xp, xq, c)));
+        publish_part<MP>(a, row0 + i, c, block_reduce<MP, false>(thread_stats<MP, kVecS>(xp, xq, c), i & 1));
 #pragma unroll
         for (int k = 0; k < kVecS; ++k) {
             xp[k] = yp[k];
