@@ -111,6 +111,8 @@ def main():
     ap.add_argument("--gen-workers", type=int, default=1,
                     help="forked processes generating the inputs; more speed up the large "
                          "workloads, but forked workers die under rocprofv3 counter collection")
+    ap.add_argument("--decoder", action="store_true",
+                    help="time rounds of the multi-round driver (B=1, K=4, V=32000) instead")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy 5 times (reference for "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE scaling)")
@@ -131,6 +133,8 @@ def main():
         print("bench.py needs a HIP device", flush=True)
         sys.exit(1)
     sv.load_library()
+    if args.decoder:
+        return decoder_bench(args)
     cfg = dict(workloads.CONFIGS[args.workload])
     mode = args.mode or ("sampled" if "sampled" in cfg["modes"] else "greedy")
     sampled = mode == "sampled"
@@ -226,6 +230,82 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the CPU oracle baseline")
         line["cpu_baseline"] = cpu_baseline(cfg, mode)
+    print(json.dumps(line), flush=True)
+
+
+def decoder_bench(args):
+    """Rounds of the multi-round driver (SpeculativeDecoder) at the card's own
+    shape, B=1, K=4, V=32000 (workload 1), with callbacks that hand back
+    device-resident rows of that workload, so that the figure is the driver
+    and the verification, not a model.  Two input sets alternate."""
+    import numpy as np
+    import torch
+    import speculative_decoding_verification_row_amd as sv
+    import workloads
+    from workloads.device import device_batch
+    cfg = workloads.CONFIGS[1]
+    K, V = cfg["K"], cfg["V"]
+    mode = args.mode or "sampled"
+    sampled = mode == "sampled"
+    dev = torch.device("cuda:0")
+    sets = [device_batch(cfg["family"], 1, K, V, seed=s, device=dev, sampled=sampled) for s in range(2)]
+    turn = [0]
+
+    def draft_step(prefix, k):
+        db = sets[turn[0] % 2]
+        return db["dt"][0], (db["dp"][0] if sampled else None)
+
+    def target_step(prefix, proposed):
+        db = sets[turn[0] % 2]
+        turn[0] += 1
+        return db["tp"][0]
+
+    dec = sv.SpeculativeDecoder(draft_step, target_step, k=K, greedy=not sampled, seed=0, device=dev)
+    dec.generate([1], max_new=args.warmup * (K + 1))
+    torch.cuda.synchronize()
+    dec.stats = sv.DecodeStats()
+    max_new = args.steps * (K + 1)
+    t0 = time.perf_counter()
+    out = dec.generate([1], max_new=max_new)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    rounds = dec.stats.rounds
+    # the verification kernel alone on the same inputs (one event pair)
+    ws = sv.workspace_for(1, K, V, sampled, dev)
+    n_out = torch.empty(1, dtype=torch.int32, device=dev)
+    x_out = torch.empty(1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def verify(db):
+        if sampled:
+            sv.sv_verify_sample_batched(db["tp"], db["dp"], db["dt"], db["u"], n_accepted=n_out,
+                                        next_token=x_out, workspace=ws, stream=stream)
+        else:
+            sv.sv_verify_greedy_batched(db["tp"], db["dt"], n_accepted=n_out, next_token=x_out,
+                                        workspace=ws, stream=stream)
+
+    for j in range(20):
+        verify(sets[j % 2])
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for j in range(rounds):
+        verify(sets[j % 2])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    kern_us = e0.elapsed_time(e1) * 1e3 / rounds
+    round_us = wall / rounds * 1e6
+    line = {
+        "metric": f"speculative decoding driver rounds/s, B=1 K={K} V={V} {mode}, device-resident callbacks",
+        "value": round(rounds / wall, 1), "unit": "rounds/s", "n_gpus": 1, "steps": rounds,
+        "warmup": args.warmup, "ms_per_step": round(round_us / 1e3, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"B=1 K={K} V={V} {mode} decoder rounds", "recipe": cfg["family"]},
+        "tokens_per_round": round((len(out) - 1) / rounds, 3),
+        "verify_launch_us": round(kern_us, 2),
+        "host_us_per_round": round(round_us - kern_us, 2),
+        "mean_accepted": round(dec.stats.mean_accepted(), 3),
+    }
     print(json.dumps(line), flush=True)
 
 

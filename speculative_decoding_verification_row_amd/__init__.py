@@ -35,6 +35,7 @@ __all__ = [
     "sv_workspace_size", "sv_workspace_init", "sv_workspace_error", "sv_status_string",
     "sv_verify_greedy_batched", "sv_verify_sample_batched",
     "verify_greedy", "verify_sample", "stats_to_numpy", "workspace_for",
+    "SpeculativeDecoder", "DecodeStats",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -264,3 +265,7 @@ def verify_sample(target_probs, draft_probs, draft_tokens, uniforms, **kw):
                                        draft_tokens.reshape(1, -1), uniforms.reshape(1, -1), **kw)
         return int(out[0].item()), int(out[1].item())
     return sv_verify_sample_batched(target_probs, draft_probs, draft_tokens, uniforms, **kw)
+
+
+# The multi-round driver (the card's SpeculativeDecoder), over the calls above.
+from .decoder import DecodeStats, SpeculativeDecoder  # noqa: E402
