@@ -65,21 +65,25 @@ def traffic_for(kernel: str, workload: str):
     return e.get("bytes_per_launch")
 
 
-def cpu_baseline(cfg, mode, target_seconds=10.0):
+def cpu_baseline(cfg, mode, target_seconds=10.0, logits=False, tau=1.0):
     """Time the fp64 oracle as it stands on this host's cores over a bounded
-    sample of the workload (whole sequences of round 0), scaled to rounds/s."""
+    sample of the workload (whole sequences of round 0), scaled to rounds/s.
+    The logits oracle is numpy on one thread."""
     import numpy as np
     import oracle
     import workloads
-    cores = workloads.default_workers()
+    cores = 1 if logits else workloads.default_workers()
     B = cfg["B"]
     n_seq = min(B, max(1, 2 * cores))
     seqs = list(range(n_seq))
-    hb = workloads.make_batch(cfg["family"], B, cfg["K"], cfg["V"], seed=0, seqs=seqs)
+    hb = workloads.make_batch(cfg["family"], B, cfg["K"], cfg["V"], seed=0, seqs=seqs, logits=logits)
     sampled = mode == "sampled"
 
     def once():
-        if sampled:
+        if logits:
+            from oracle.logits import verify_sample_logits
+            verify_sample_logits(hb.target_probs, hb.draft_probs, hb.draft_tokens, hb.uniforms, tau)
+        elif sampled:
             oracle.verify_sample(hb.target_probs, hb.draft_probs, hb.draft_tokens, hb.uniforms,
                                  threads=cores, diagnostics=False)
         else:
@@ -111,6 +115,9 @@ def main():
     ap.add_argument("--gen-workers", type=int, default=1,
                     help="forked processes generating the inputs; more speed up the large "
                          "workloads, but forked workers die under rocprofv3 counter collection")
+    ap.add_argument("--logits", action="store_true",
+                    help="sampled verification given logits (warped in the library) instead of probabilities")
+    ap.add_argument("--temperature", type=float, default=1.0, help="temperature of --logits")
     ap.add_argument("--decoder", action="store_true",
                     help="time rounds of the multi-round driver (B=1, K=4, V=32000) instead")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -137,16 +144,20 @@ def main():
         return decoder_bench(args)
     cfg = dict(workloads.CONFIGS[args.workload])
     mode = args.mode or ("sampled" if "sampled" in cfg["modes"] else "greedy")
+    if args.logits:
+        if cfg["family"] not in ("c1", "c3"):
+            raise SystemExit("--logits takes workload 1 or 3 (families with logits)")
+        mode = "sampled"
     sampled = mode == "sampled"
     B, K, V = cfg["B"], cfg["K"], cfg["V"]
     dev = torch.device("cuda:0")
-    workload = f"B={B} K={K} V={V} {mode}"
+    workload = f"B={B} K={K} V={V} {mode}" + (f" logits tau={args.temperature:g}" if args.logits else "")
     log(f"workload {args.workload}: {workload}; generating {args.sets} input sets")
 
     sets = []
     for s in range(args.sets):
         sets.append(device_batch(cfg["family"], B, K, V, seed=s, device=dev, sampled=sampled,
-                                 workers=args.gen_workers))
+                                 workers=args.gen_workers, logits=args.logits))
         log(f"  set {s} ready ({sets[-1]['sha256'][:12]})")
     n_out = torch.empty(B, dtype=torch.int32, device=dev)
     x_out = torch.empty(B, dtype=torch.int32, device=dev)
@@ -154,7 +165,10 @@ def main():
     ws = sv.workspace_for(B, K, V, sampled, dev, stream)
 
     def step(db):
-        if sampled:
+        if args.logits:
+            sv.sv_verify_sample_logits_batched(db["tp"], db["dp"], db["dt"], db["u"], args.temperature,
+                                               n_accepted=n_out, next_token=x_out, workspace=ws, stream=stream)
+        elif sampled:
             sv.sv_verify_sample_batched(db["tp"], db["dp"], db["dt"], db["u"], n_accepted=n_out,
                                         next_token=x_out, workspace=ws, stream=stream)
         else:
@@ -184,11 +198,12 @@ def main():
 
     # spot check of the last step's outputs against the oracle (2 sequences)
     last = sets[(args.steps - 1) % len(sets)]
-    spot = spot_check(cfg, mode, last, n_out, x_out, seed=(args.steps - 1) % len(sets))
+    spot = spot_check(cfg, mode, last, n_out, x_out, seed=(args.steps - 1) % len(sets),
+                      logits=args.logits, tau=args.temperature)
 
     fbytes = workloads.formula_bytes(B, K, V, sampled)
     achieved = fbytes / (avg_ms * 1e-3) / 1e9
-    kernel = "sv_sample_kernel" if sampled else "sv_greedy_kernel"
+    kernel = "sv_logits_kernel" if args.logits else ("sv_sample_kernel" if sampled else "sv_greedy_kernel")
     rounds_per_s = args.steps / wall
     line = {
         "metric": f"verify rounds/s + HBM GB/s (% of peak), {workload}",
@@ -229,7 +244,7 @@ def main():
         line["copy_calibration_bytes"] = src.numel() * 4
     if not args.no_cpu_baseline:
         log("timing the CPU oracle baseline")
-        line["cpu_baseline"] = cpu_baseline(cfg, mode)
+        line["cpu_baseline"] = cpu_baseline(cfg, mode, logits=args.logits, tau=args.temperature)
     print(json.dumps(line), flush=True)
 
 
@@ -309,15 +324,20 @@ def decoder_bench(args):
     print(json.dumps(line), flush=True)
 
 
-def spot_check(cfg, mode, db, n_out, x_out, seed):
+def spot_check(cfg, mode, db, n_out, x_out, seed, logits=False, tau=1.0):
     import numpy as np
     import oracle
     import workloads
     seqs = [0, cfg["B"] - 1]
-    hb = workloads.make_batch(cfg["family"], cfg["B"], cfg["K"], cfg["V"], seed=seed, seqs=seqs)
+    hb = workloads.make_batch(cfg["family"], cfg["B"], cfg["K"], cfg["V"], seed=seed, seqs=seqs, logits=logits)
     n = n_out.cpu().numpy()[seqs]
     x = x_out.cpu().numpy()[seqs]
-    if mode == "sampled":
+    if logits:
+        from oracle.logits import verify_sample_logits
+        o = verify_sample_logits(hb.target_probs, hb.draft_probs, hb.draft_tokens, hb.uniforms, tau)
+        d = o["diag"]
+        bnd = (d["accept_margin"] <= 1e-5) | (d["draw_margin"] <= 1e-5)
+    elif mode == "sampled":
         o = oracle.verify_sample(hb.target_probs, hb.draft_probs, hb.draft_tokens, hb.uniforms)
         d = o["diag"]
         bnd = (d["accept_margin"] <= 1e-5) | (d["draw_margin"] <= 1e-5)

@@ -120,6 +120,26 @@ sv_status sv_verify_sample_batched(const float* target_probs, const float* draft
                                    void* workspace, size_t workspace_bytes,
                                    sv_row_stats* stats, void* stream);
 
+/* Sampled verification on logits, warped by one temperature (the card's
+ * speculative-sampling bullet holds when target and draft are warped
+ * identically; here the library warps both).  target_logits [B, K+1, V] and
+ * draft_logits [B, K, V] are f32 logits, finite; the warped distribution of
+ * a row l is softmax(l / temperature), and verification is then that of
+ * sv_verify_sample_batched on the warped rows: accept t_i iff
+ * u_i * w_q(t_i) * P_i < w_p(t_i) * Q_i, with w(x) = exp((l(x) - max l) / tau)
+ * (fp32) and the masses P, Q its fp64 sums; the residual and the draws use
+ * the same weights.  One pass over the logits: each chunk publishes its
+ * maximum and its weight sum against it, and readers rescale to the row's
+ * maximum.  No row statistics.  The workspace is that of the sampled call
+ * (sv_workspace_size(B, K, V, 1)).
+ * Errors: those of the sampled call, and SV_ERR_INVALID_ARG for a temperature
+ * that is not finite and > 0. */
+sv_status sv_verify_sample_logits_batched(const float* target_logits, const float* draft_logits,
+                                          const int32_t* draft_tokens, const float* uniforms, float temperature,
+                                          int32_t B, int32_t K, int32_t V,
+                                          int32_t* n_accepted, int32_t* next_token,
+                                          void* workspace, size_t workspace_bytes, void* stream);
+
 /* Synchronously read the workspace's device-fault word into *error_out
  * (host memory), waiting for `stream` first: 0 when every call since the
  * last sv_workspace_init completed normally.  The current kernels never set

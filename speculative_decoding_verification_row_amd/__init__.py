@@ -33,7 +33,7 @@ import torch
 __all__ = [
     "SVError", "ROW_STATS_DTYPE", "library_path", "load_library",
     "sv_workspace_size", "sv_workspace_init", "sv_workspace_error", "sv_status_string",
-    "sv_verify_greedy_batched", "sv_verify_sample_batched",
+    "sv_verify_greedy_batched", "sv_verify_sample_batched", "sv_verify_sample_logits_batched",
     "verify_greedy", "verify_sample", "stats_to_numpy", "workspace_for",
     "SpeculativeDecoder", "DecodeStats",
 ]
@@ -85,6 +85,8 @@ def load_library():
     lib.sv_verify_greedy_batched.restype = ctypes.c_int
     lib.sv_verify_sample_batched.argtypes = [P, P, P, P, I32, I32, I32, P, P, P, SZ, P, P]
     lib.sv_verify_sample_batched.restype = ctypes.c_int
+    lib.sv_verify_sample_logits_batched.argtypes = [P, P, P, P, ctypes.c_float, I32, I32, I32, P, P, P, SZ, P]
+    lib.sv_verify_sample_logits_batched.restype = ctypes.c_int
     lib.sv_workspace_error.argtypes = [P, ctypes.POINTER(I32), P]
     lib.sv_workspace_error.restype = ctypes.c_int
     lib.sv_status_string.argtypes = [ctypes.c_int]
@@ -239,6 +241,35 @@ def sv_verify_sample_batched(target_probs: torch.Tensor, draft_probs: torch.Tens
     if rc != SV_OK:
         raise SVError(rc, "sv_verify_sample_batched")
     return (n_accepted, next_token, st) if st is not None else (n_accepted, next_token)
+
+
+def sv_verify_sample_logits_batched(target_logits: torch.Tensor, draft_logits: torch.Tensor,
+                                    draft_tokens: torch.Tensor, uniforms: torch.Tensor, temperature: float,
+                                    n_accepted=None, next_token=None, workspace=None, stream=None):
+    """Sampled verification of B sequences given logits, both warped by
+    softmax(l / temperature) inside the library.
+
+    target_logits [B, K+1, V] f32, draft_logits [B, K, V] f32, draft_tokens
+    [B, K] int32, uniforms [B, K+1] f32 in [0, 1) (CUDA).  Returns
+    (n_accepted, next_token)."""
+    B, K1, V = target_logits.shape
+    K = K1 - 1
+    dev = target_logits.device
+    _check(target_logits, "target_logits", torch.float32, (B, K1, V), dev)
+    _check(draft_logits, "draft_logits", torch.float32, (B, K, V), dev)
+    _check(draft_tokens, "draft_tokens", torch.int32, (B, K), dev)
+    _check(uniforms, "uniforms", torch.float32, (B, K1), dev)
+    n_accepted, next_token = _outputs(B, dev, n_accepted, next_token)
+    with torch.cuda.device(dev):
+        if workspace is None:
+            workspace = workspace_for(B, K, V, True, dev, stream)
+        rc = load_library().sv_verify_sample_logits_batched(
+            _ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens), _ptr(uniforms),
+            ctypes.c_float(float(temperature)), B, K, V, _ptr(n_accepted), _ptr(next_token),
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream_ptr(stream, dev))
+    if rc != SV_OK:
+        raise SVError(rc, "sv_verify_sample_logits_batched")
+    return n_accepted, next_token
 
 
 def stats_to_numpy(stats: torch.Tensor) -> np.ndarray:

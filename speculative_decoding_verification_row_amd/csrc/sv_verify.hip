@@ -127,6 +127,7 @@ struct Args {
     int force_recompute;             // test hook: readers recompute every partial
     int walk_rows;                   // greedy: rows per walk
     unsigned long long poll_ticks;   // wait bound in wall-clock ticks
+    float ktau;                      // logits: log2(e) / temperature
 };
 
 // ------------------------------------------- cross-block communication --
@@ -1350,6 +1351,766 @@ __global__ __launch_bounds__(kThreads, 4) void sv_sample_kernel(Args a)
     if (threadIdx.x == 0) put_u64(&a.sstate[b], tag_state(state >= 0 ? state + 1 : 0, a.epoch));
 }
 
+// ------------------------------------------------------------ logits --
+//
+// Sampled verification on logits warped by a temperature tau.  The warped
+// distribution of a row of logits l is softmax(l / tau); the card asks that
+// target and draft be warped identically, and one tau warps both here.  The
+// work decomposition, the walk and the finishing are those of
+// sv_sample_kernel; what a chunk publishes differs.  A chunk first takes the
+// block-wide maximum m_c of its target values and of its draft values
+// (positions at or past V left out), then sums the weights
+// exp((l - m_c) / tau) = exp2((l - m_c) * k), k = log2(e) / tau, each in
+// fp32, summed in fp64 in the thread order of the probability pass, and
+// publishes (m_c, s_c) per operand.  A reader of a row takes its maximum M
+// (the largest m_c) and its mass sum_c s_c exp2((m_c - M) * k), in chunk
+// order.  Single weights (p(t), q(t), the residual, the draws) are
+// exp2((l - M) * k) against the same M, on the scale of that mass.
+
+__device__ __forceinline__ float lweight(float l, float m, float k)
+{
+    return __builtin_amdgcn_exp2f((l - m) * k);
+}
+
+// Maximum over the wave (all 64 lanes active), the same in every lane.
+__device__ __forceinline__ float wave_maxf(float v)
+{
+    v = fmaxf(v, __int_as_float(dpp_i32<kDppPairs>(__float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp_i32<kDppQuads>(__float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp_i32<kDppHalfMirror>(__float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp_i32<kDppMirror>(__float_as_int(v))));
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+// Whether every position of chunk c lies below V (no masking needed).
+template <int NV>
+__device__ __forceinline__ bool chunk_full(int c, int V)
+{
+    return (int64_t)(c + 1) * (kThreads * NV * 4) <= (int64_t)V;
+}
+
+// Largest logit of the thread's share of chunk c (positions < V); -inf if none.
+template <int NV>
+__device__ __forceinline__ float share_max(const float4 (&v)[NV], int c, int V, bool full)
+{
+    float m = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+        const int p0 = 4 * f4_index<NV>(c, k);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (full || p0 + e < V) m = fmaxf(m, comp(v[k], e));
+    }
+    return m;
+}
+
+// Sum of the weights of the thread's share against m (fp64; k, then e, ascending).
+template <int NV>
+__device__ __forceinline__ double share_wsum(const float4 (&v)[NV], int c, int V, bool full, float m, float k)
+{
+    double s = 0.0;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int p0 = 4 * f4_index<NV>(c, j);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (full || p0 + e < V) s += (double)lweight(comp(v[j], e), m, k);
+    }
+    return s;
+}
+
+// Block maxima of a and b, in every thread.  Consecutive calls alternate
+// `slot`, as for block_reduce.
+__device__ __forceinline__ void block_max2(float& a, float& b, int slot)
+{
+    __shared__ float s_a[2][kWaves], s_b[2][kWaves];
+    a = wave_maxf(a);
+    b = wave_maxf(b);
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    if (lane == 0) {
+        s_a[slot][w] = a;
+        s_b[slot][w] = b;
+    }
+    __syncthreads();
+    a = fmaxf(fmaxf(s_a[slot][0], s_a[slot][1]), fmaxf(s_a[slot][2], s_a[slot][3]));
+    b = fmaxf(fmaxf(s_b[slot][0], s_b[slot][1]), fmaxf(s_b[slot][2], s_b[slot][3]));
+}
+
+struct LStat {
+    float mp, mq;      // chunk maxima (every thread)
+    double sp, sq;     // weight sums against them (thread 0)
+};
+
+// Block-cooperative: (m_c, s_c) of target chunk pv and, with Q, of draft
+// chunk qv.  Consecutive calls alternate `slot`.
+template <int NV, bool Q>
+__device__ __forceinline__ LStat chunk_stats_l(const float4 (&pv)[NV], const float4 (&qv)[NV], int c, int V,
+                                               float k, int slot)
+{
+    const bool full = chunk_full<NV>(c, V);
+    float mp = share_max<NV>(pv, c, V, full);
+    float mq = Q ? share_max<NV>(qv, c, V, full) : -INFINITY;
+    block_max2(mp, mq, slot);
+    Acc t{0.0, 0.0, 0.0, -INFINITY, 0};
+    t.sp = share_wsum<NV>(pv, c, V, full, mp, k);
+    if (Q) t.sq = share_wsum<NV>(qv, c, V, full, mq, k);
+    const Acc r = block_reduce<Q ? (kSP | kSQ) : kSP, false>(t, slot);
+    return LStat{mp, mq, r.sp, r.sq};
+}
+
+// Publish a chunk's (m, s): sums as tagged fp64 words (sp, sq), maxima as
+// tagged (value, 0) words in the am (target) and smin (draft) slots.
+__device__ __forceinline__ void publish_l(const Args& a, int64_t row, int c, const LStat& s, bool q)
+{
+    if (threadIdx.x == 0) {
+        Part* dst = &a.parts[row * a.NC + c];
+        put_u64(&dst->sp, tag_f64(s.sp, a.epoch));
+        put_u64(&dst->am, tag_am(s.mp, 0, a.epoch));
+        if (q) {
+            put_u64(&dst->sq, tag_f64(s.sq, a.epoch));
+            put_u64(&dst->smin, tag_am(s.mq, 0, a.epoch));
+        }
+    }
+}
+
+// Wave-cooperative: a row's maximum and mass from the chunks a lane holds
+// (chunks l and l + 64; m = -inf for none): M is the largest m, the mass is
+// sum_c s_c exp2((m_c - M) k), a lane's pair first, then the fixed wave sum.
+// Every reader of a row uses this.
+__device__ __forceinline__ double chunk_scaled(float m, double s, float M, float k)
+{
+    return m == -INFINITY ? 0.0 : s * (double)lweight(m, M, k);
+}
+__device__ __forceinline__ double row_mass_l(float m0, double s0, float m1, double s1, float k, float* Mout)
+{
+    const float M = wave_maxf(fmaxf(m0, m1));
+    *Mout = M;
+    return wave_sum(chunk_scaled(m0, s0, M, k) + chunk_scaled(m1, s1, M, k));
+}
+
+// Residual mass of one position: max(0, w_p Q - w_q P), fp64.
+__device__ __forceinline__ double resid_l(float lp, float lq, double P, double Q, float Mp, float Mq, float k)
+{
+    const double d = (double)lweight(lp, Mp, k) * Q - (double)lweight(lq, Mq, k) * P;
+    return d > 0.0 ? d : 0.0;
+}
+
+struct LRow {
+    double P, Q;
+    float Mp, Mq;
+};
+
+// The walk's poll of row i: lane c < min(NC, 64) of wave 0 reads chunk c's
+// four words; lane 0 also the logits at the draft token and the uniform.
+struct PollL {
+    unsigned long long sp, sq, mp, mq;
+    float pt, qt, u;
+    int tin;
+};
+
+__device__ __forceinline__ PollL poll_issue_l(const Args& a, int b, int i, int tok)
+{
+    PollL p{0ull, 0ull, 0ull, 0ull, 0.0f, 0.0f, 0.0f, 0};
+    const int t = threadIdx.x, K = a.K, V = a.V;
+    const int64_t row = (int64_t)b * (K + 1) + i;
+    if (t < a.NC && t < 64) {
+        const Part* pp = a.parts + row * a.NC + t;
+        p.sp = get_u64(&pp->sp);
+        p.sq = get_u64(&pp->sq);
+        p.mp = get_u64(&pp->am);
+        p.mq = get_u64(&pp->smin);
+    }
+    if (t == 0) {
+        p.tin = tok >= 0 && tok < V;
+        p.pt = p.tin ? a.tp[row * V + tok] : 0.0f;
+        p.qt = p.tin ? a.dp[((int64_t)b * K + i) * V + tok] : 0.0f;
+        p.u = a.u[row];
+    }
+    return p;
+}
+
+__device__ __forceinline__ bool lwords_ok(unsigned long long sp, unsigned long long sq, unsigned long long mp,
+                                          unsigned long long mq, unsigned ep)
+{
+    return f64_ok(sp, ep) && f64_ok(sq, ep) && am_ok(mp, ep) && am_ok(mq, ep);
+}
+
+// Block-cooperative (wave 0 decides, as in poll_decide): the masses and
+// maxima of row i and the acceptance of its draft token.  Returns 0, 1, or
+// -1 when some word is still missing at the wait bound.  Uniform result.
+__device__ int poll_decide_l(const Args& a, int b, int i, PollL pl, LRow* out)
+{
+    __shared__ LRow s_row;
+    __shared__ int s_rej;
+    const int NC = a.NC, t = threadIdx.x;
+    const unsigned ep = a.epoch;
+    const float k = a.ktau;
+    const int64_t row = (int64_t)b * (a.K + 1) + i;
+    if (t < 64) {
+        const Part* p0 = a.parts + row * NC + t;
+        const Part* p1 = p0 + 64;
+        bool need0 = t < NC, need1 = t + 64 < NC;
+        unsigned long long w1[4] = {0ull, 0ull, 0ull, 0ull};
+        if (need1) {
+            w1[0] = get_u64(&p1->sp);
+            w1[1] = get_u64(&p1->sq);
+            w1[2] = get_u64(&p1->am);
+            w1[3] = get_u64(&p1->smin);
+        }
+        float m0p = -INFINITY, m0q = -INFINITY, m1p = -INFINITY, m1q = -INFINITY;
+        double s0p = 0.0, s0q = 0.0, s1p = 0.0, s1q = 0.0;
+        const unsigned long long t0 = wall_clock64();
+        for (;;) {
+            if (need0 && lwords_ok(pl.sp, pl.sq, pl.mp, pl.mq, ep) && !a.force_recompute) {
+                s0p = f64_of(pl.sp);
+                s0q = f64_of(pl.sq);
+                m0p = am_val(pl.mp);
+                m0q = am_val(pl.mq);
+                need0 = false;
+            }
+            if (need1 && lwords_ok(w1[0], w1[1], w1[2], w1[3], ep) && !a.force_recompute) {
+                s1p = f64_of(w1[0]);
+                s1q = f64_of(w1[1]);
+                m1p = am_val(w1[2]);
+                m1q = am_val(w1[3]);
+                need1 = false;
+            }
+            if (__ballot(need0 || need1) == 0ull) break;
+            if (a.force_recompute || wall_clock64() - t0 > a.poll_ticks) break;
+            __builtin_amdgcn_s_sleep(2);
+            if (need0) {
+                pl.sp = get_u64(&p0->sp);
+                pl.sq = get_u64(&p0->sq);
+                pl.mp = get_u64(&p0->am);
+                pl.mq = get_u64(&p0->smin);
+            }
+            if (need1) {
+                w1[0] = get_u64(&p1->sp);
+                w1[1] = get_u64(&p1->sq);
+                w1[2] = get_u64(&p1->am);
+                w1[3] = get_u64(&p1->smin);
+            }
+        }
+        if (__ballot(need0 || need1) == 0ull) {
+            LRow r;
+            r.P = row_mass_l(m0p, s0p, m1p, s1p, k, &r.Mp);
+            r.Q = row_mass_l(m0q, s0q, m1q, s1q, k, &r.Mq);
+            if (t == 0) {
+                const float ept = pl.tin ? lweight(pl.pt, r.Mp, k) : 0.0f;
+                const float eqt = pl.tin ? lweight(pl.qt, r.Mq, k) : 0.0f;
+                s_row = r;
+                s_rej = accepted(pl.u, ept, eqt, r.P, r.Q) ? 0 : 1;
+            }
+        } else if (t == 0) {
+            s_rej = -1;
+        }
+    }
+    __syncthreads();
+    *out = s_row;
+    return s_rej;
+}
+
+// Residual mass of the thread's parked share (k, then e, ascending).
+__device__ __forceinline__ double parked_resid_l(const LRow& r, float k, int c, int V)
+{
+    const bool full = chunk_full<kVecS>(c, V);
+    double w = 0.0;
+#pragma unroll
+    for (int j = 0; j < kVecS; ++j) {
+        const f32x4 p = lds.parked[j][threadIdx.x], q = lds.parked[kVecS + j][threadIdx.x];
+        const int p0 = 4 * f4_index<kVecS>(c, j);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (full || p0 + e < V) w += resid_l(p[e], q[e], r.P, r.Q, r.Mp, r.Mq, k);
+    }
+    return w;
+}
+
+// The same sum re-reading the chunk (same order).
+template <bool VEC>
+__device__ __forceinline__ double thread_resid_reload_l(Row prow, Row qrow, int c, int V, const LRow& r, float k)
+{
+    const bool full = chunk_full<kVecS>(c, V);
+    double w = 0.0;
+    for (int j = 0; j < kVecS; ++j) {
+        const float4 p4 = load_one<VEC, kVecS>(prow, c, j), q4 = load_one<VEC, kVecS>(qrow, c, j);
+        const int p0 = 4 * f4_index<kVecS>(c, j);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (full || p0 + e < V) w += resid_l(comp(p4, e), comp(q4, e), r.P, r.Q, r.Mp, r.Mq, k);
+    }
+    return w;
+}
+
+// Block-cooperative: the residual chunk masses of row n into m[0..NC),
+// recomputing missing ones and ones published as NaN.
+template <bool VEC>
+__device__ void gather_resid_l(const Args& a, int b, int n, const LRow& r, double* m)
+{
+    __shared__ unsigned long long s_miss[2];
+    const int NC = a.NC, K = a.K, V = a.V;
+    const unsigned ep = a.epoch;
+    const unsigned long long* wp = a.wpart + ((int64_t)b * K + n) * NC;
+    const int c = threadIdx.x;
+    bool need = c < NC, redo = false;
+    const unsigned long long t0 = wall_clock64();
+    for (;;) {
+        bool any = false;
+        if (need) {
+            const unsigned long long wv = get_u64(&wp[c]);
+            if (f64_ok(wv, ep) && !a.force_recompute) {
+                m[c] = f64_of(wv);
+                need = false;
+                if (m[c] != m[c]) redo = true;
+            } else {
+                any = true;
+            }
+        }
+        if (!__syncthreads_or(any)) break;
+        if (wait_expired(a, t0)) break;
+        __builtin_amdgcn_s_sleep(2);
+    }
+    if (!__syncthreads_or(need || redo)) return;
+    if (threadIdx.x < 2) s_miss[threadIdx.x] = 0ull;
+    __syncthreads();
+    if (need || redo) atomicOr(&s_miss[c >> 6], 1ull << (c & 63));   // LDS
+    __syncthreads();
+    const Row prow = row_of(a.tp + ((int64_t)b * (K + 1) + n) * V, V);
+    const Row qrow = row_of(a.dp + ((int64_t)b * K + n) * V, V);
+    for (int h = 0; h < 2; ++h) {
+        unsigned long long mk = s_miss[h];
+        while (mk) {
+            const int cc = h * 64 + __ffsll((unsigned long long)mk) - 1;
+            mk &= mk - 1;
+            const double w = block_sum(thread_resid_reload_l<VEC>(prow, qrow, cc, V, r, a.ktau));
+            if (threadIdx.x == 0) {
+                m[cc] = strip8(w);
+                put_u32(&a.hdr->slow_path, 1u);
+            }
+        }
+    }
+    __syncthreads();
+}
+
+// Block-cooperative: the maxima and masses of row i of sequence b (with Q,
+// also its draft row), and its chunks' masses scaled to the row maximum in
+// ms[0..NC) (target).  Words that do not carry this call's tag within the
+// wait bound are recomputed from the inputs, bit-identically.
+template <bool VEC, bool Q>
+__device__ LRow gather_row_l(const Args& a, int b, int i, double* ms)
+{
+    __shared__ float s_mp[kMaxNC], s_mq[kMaxNC];
+    __shared__ double s_sp[kMaxNC], s_sq[kMaxNC];
+    __shared__ unsigned long long s_miss[2];
+    __shared__ LRow s_row;
+    const int NC = a.NC, K = a.K, V = a.V, c = threadIdx.x;
+    const unsigned ep = a.epoch;
+    const int64_t row = (int64_t)b * (K + 1) + i;
+    bool need = c < NC;
+    const unsigned long long t0 = wall_clock64();
+    for (;;) {
+        bool any = false;
+        if (need) {
+            const Part* pp = a.parts + row * NC + c;
+            const unsigned long long sp = get_u64(&pp->sp), mp = get_u64(&pp->am);
+            const unsigned long long sq = Q ? get_u64(&pp->sq) : 0ull, mq = Q ? get_u64(&pp->smin) : 0ull;
+            const bool ok = f64_ok(sp, ep) && am_ok(mp, ep) && (!Q || (f64_ok(sq, ep) && am_ok(mq, ep)));
+            if (ok && !a.force_recompute) {
+                s_sp[c] = f64_of(sp);
+                s_mp[c] = am_val(mp);
+                if (Q) {
+                    s_sq[c] = f64_of(sq);
+                    s_mq[c] = am_val(mq);
+                }
+                need = false;
+            } else {
+                any = true;
+            }
+        }
+        if (!__syncthreads_or(any)) break;
+        if (wait_expired(a, t0)) break;
+        __builtin_amdgcn_s_sleep(2);
+    }
+    if (__syncthreads_or(need)) {   // recompute what is missing (rare), one chunk at a time
+        if (threadIdx.x < 2) s_miss[threadIdx.x] = 0ull;
+        __syncthreads();
+        if (need) atomicOr(&s_miss[c >> 6], 1ull << (c & 63));   // LDS
+        __syncthreads();
+        const Row prow = row_of(a.tp + row * V, V);
+        const Row qrow = Q ? row_of(a.dp + ((int64_t)b * K + i) * V, V) : prow;
+        int slot = 0;
+        for (int h = 0; h < 2; ++h) {
+            unsigned long long mk = s_miss[h];
+            while (mk) {
+                const int cc = h * 64 + __ffsll((unsigned long long)mk) - 1;
+                mk &= mk - 1;
+                float4 pv[kVecS], qv[kVecS];
+#pragma unroll
+                for (int j = 0; j < kVecS; ++j) {
+                    pv[j] = load_one<VEC, kVecS>(prow, cc, j);
+                    qv[j] = Q ? load_one<VEC, kVecS>(qrow, cc, j) : pv[j];
+                }
+                const LStat st = chunk_stats_l<kVecS, Q>(pv, qv, cc, V, a.ktau, slot);
+                slot ^= 1;
+                if (threadIdx.x == 0) {
+                    s_sp[cc] = strip8(st.sp);
+                    s_mp[cc] = st.mp;
+                    if (Q) {
+                        s_sq[cc] = strip8(st.sq);
+                        s_mq[cc] = st.mq;
+                    }
+                    put_u32(&a.hdr->slow_path, 1u);
+                }
+            }
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x < 64) {
+        const int l = threadIdx.x;
+        const float m0 = l < NC ? s_mp[l] : -INFINITY, m1 = l + 64 < NC ? s_mp[l + 64] : -INFINITY;
+        const double x0 = l < NC ? s_sp[l] : 0.0, x1 = l + 64 < NC ? s_sp[l + 64] : 0.0;
+        LRow r{0.0, 0.0, 0.0f, 0.0f};
+        r.P = row_mass_l(m0, x0, m1, x1, a.ktau, &r.Mp);
+        if (l < NC) ms[l] = chunk_scaled(m0, x0, r.Mp, a.ktau);
+        if (l + 64 < NC) ms[l + 64] = chunk_scaled(m1, x1, r.Mp, a.ktau);
+        if (Q) {
+            const float n0 = l < NC ? s_mq[l] : -INFINITY, n1 = l + 64 < NC ? s_mq[l + 64] : -INFINITY;
+            const double y0 = l < NC ? s_sq[l] : 0.0, y1 = l + 64 < NC ? s_sq[l + 64] : 0.0;
+            r.Q = row_mass_l(n0, y0, n1, y1, a.ktau, &r.Mq);
+        }
+        if (l == 0) s_row = r;
+    }
+    __syncthreads();
+    return s_row;
+}
+
+// Search of chunk c (the chunk_draw search) with logit weights: the residual
+// max(0, w_p Q - w_q P) (RESID) or w_p, against the row maxima; positions at
+// or past V weigh 0.
+template <bool VEC, bool RESID>
+__device__ __forceinline__ int chunk_draw_l(Row prow, Row qrow, const LRow& r, float k, int V, int c, double base,
+                                            double T)
+{
+    constexpr int NV = kVecS;
+    __shared__ double s_seg[NV][kWaves];
+    __shared__ int s_ks, s_ws;
+    __shared__ double s_base;
+    __shared__ int s_x;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    auto wt = [&](float p, float q, int pos) -> double {
+        if (pos >= V) return 0.0;
+        return RESID ? resid_l(p, q, r.P, r.Q, r.Mp, r.Mq, k) : (double)lweight(p, r.Mp, k);
+    };
+    float4 pv[NV], qv[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        pv[j] = load_one<VEC, NV>(prow, c, j);
+        qv[j] = RESID ? load_one<VEC, NV>(qrow, c, j) : pv[j];
+    }
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int p0 = 4 * f4_index<NV>(c, j);
+        double t = 0.0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) t += wt(comp(pv[j], e), comp(qv[j], e), p0 + e);
+        const double s = wave_sum(t);
+        if (lane == 0) s_seg[j][w] = s;
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) {
+        constexpr int kSegs = NV * kWaves;
+        const int q = threadIdx.x;
+        const double s = q < kSegs ? s_seg[q / kWaves][q % kWaves] : 0.0;
+        const double incl = wave_inclusive_scan(s);
+        double excl = __shfl_up(incl, 1);
+        if (q == 0) excl = 0.0;
+        const double run = base + excl;
+        const unsigned long long mh = __ballot(q < kSegs && run + s > T);
+        const unsigned long long mp = __ballot(q < kSegs && s > 0.0);
+        const int sel = mh ? __ffsll((unsigned long long)mh) - 1 : (mp ? 63 - __clzll(mp) : 0);
+        const double bs = __shfl(run, sel);
+        if (q == 0) {
+            s_ks = sel / kWaves;
+            s_ws = sel % kWaves;
+            s_base = bs;
+        }
+    }
+    __syncthreads();
+    if (w == s_ws) {
+        const int j = s_ks;
+        float4 p4 = pv[0], q4 = qv[0];
+#pragma unroll
+        for (int jj = 1; jj < NV; ++jj)
+            if (jj == j) {
+                p4 = pv[jj];
+                q4 = qv[jj];
+            }
+        const int p0 = 4 * f4_index<NV>(c, j);
+        double vv[4], tot = 0.0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            vv[e] = wt(comp(p4, e), comp(q4, e), p0 + e);
+            tot += vv[e];
+        }
+        const double incl = wave_inclusive_scan(tot);
+        double run = __shfl_up(incl, 1);
+        if (lane == 0) run = 0.0;
+        run += s_base;
+        int hit = -1, lastpos = -1;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            run += vv[e];
+            if (hit < 0 && run > T) hit = e;
+            if (vv[e] > 0.0) lastpos = e;
+        }
+        const unsigned long long mh = __ballot(hit >= 0);
+        if (mh) {
+            const int l = __ffsll((unsigned long long)mh) - 1;
+            if (lane == l) s_x = p0 + hit;
+        } else {
+            const unsigned long long mp = __ballot(lastpos >= 0);
+            if (mp) {
+                const int l = 63 - __clzll(mp);
+                if (lane == l) s_x = p0 + lastpos;
+            } else if (lane == 0) {
+                s_x = p0;   // unreachable for a segment with mass
+            }
+        }
+    }
+    __syncthreads();
+    return s_x;
+}
+
+// Block-cooperative: the final draw of sequence b once n and row n's masses
+// are known (r: row n; for n == K only its target part is read), and the
+// outputs.  n < K: the residual of row n, located by the published residual
+// chunk masses; n == K (or a rejection that left no residual mass): the
+// warped target row n, located by its scaled chunk masses.
+template <bool VEC>
+__device__ void draw_and_write_l(const Args& a, int b, int n, LRow r)
+{
+    __shared__ double s_m[kMaxNC];
+    __shared__ int s_owner, s_resid;
+    __shared__ double s_base, s_T;
+    const int NC = a.NC, K = a.K, V = a.V;
+    const int64_t row0 = (int64_t)b * (K + 1);
+    const double uK = (double)a.u[row0 + K];
+    const Row prow = row_of(a.tp + (row0 + n) * V, V);
+    const Row qrow = n < K ? row_of(a.dp + ((int64_t)b * K + n) * V, V) : prow;
+    if (n < K) gather_resid_l<VEC>(a, b, n, r, s_m);
+    if (threadIdx.x < 64) {
+        int owner = -1;
+        double base = 0.0, T = 0.0, W = 0.0;
+        if (n < K) W = locate_chunk(s_m, NC, uK, &owner, &base, &T);
+        if (threadIdx.x == 0) {
+            s_owner = owner;
+            s_base = base;
+            s_T = T;
+            s_resid = (n < K && W > 0.0) ? 1 : 0;
+        }
+    }
+    __syncthreads();
+    const int resid_draw = s_resid;
+    if (!resid_draw) {
+        const LRow rp = gather_row_l<VEC, false>(a, b, n, s_m);
+        r.Mp = rp.Mp;
+        if (threadIdx.x < 64) {
+            int owner;
+            double base, T;
+            locate_chunk(s_m, NC, uK, &owner, &base, &T);
+            if (threadIdx.x == 0) {
+                s_owner = owner;
+                s_base = base;
+                s_T = T;
+            }
+        }
+        __syncthreads();
+    }
+    int x = -1;
+    if (s_owner >= 0)
+        x = resid_draw ? chunk_draw_l<VEC, true>(prow, qrow, r, a.ktau, V, s_owner, s_base, s_T)
+                       : chunk_draw_l<VEC, false>(prow, prow, r, a.ktau, V, s_owner, s_base, s_T);
+    if (threadIdx.x == 0) {
+        a.n_out[b] = n;
+        a.next_out[b] = x;
+    }
+    __syncthreads();
+}
+
+// Block-cooperative, for a sequence whose walks could not decide: the
+// decisions from the gathered (or recomputed) partials, then the draw.
+template <bool VEC>
+__device__ void finish_rows_l(const Args& a, int b)
+{
+    __shared__ double s_unused[kMaxNC];
+    __shared__ int s_rej;
+    const int K = a.K, V = a.V;
+    const int64_t row0 = (int64_t)b * (K + 1);
+    LRow rn{0.0, 0.0, 0.0f, 0.0f};
+    int n = K;
+    for (int i = 0; i < K; ++i) {
+        const LRow r = gather_row_l<VEC, true>(a, b, i, s_unused);
+        if (threadIdx.x == 0) {
+            const int tk = a.dt[(int64_t)b * K + i];
+            const bool tin = tk >= 0 && tk < V;
+            const float ept = tin ? lweight(a.tp[(row0 + i) * V + tk], r.Mp, a.ktau) : 0.0f;
+            const float eqt = tin ? lweight(a.dp[((int64_t)b * K + i) * V + tk], r.Mq, a.ktau) : 0.0f;
+            s_rej = accepted(a.u[row0 + i], ept, eqt, r.P, r.Q) ? 0 : 1;
+        }
+        __syncthreads();
+        const int rej = s_rej;
+        __syncthreads();
+        if (rej) {
+            n = i;
+            rn = r;
+            break;
+        }
+    }
+    draw_and_write_l<VEC>(a, b, n, rn);
+}
+
+// Block-cooperative: the outcome the walks of sequence b published (n + 1,
+// or 0 when they could not decide), or 0 when it does not arrive within the
+// wait bound.
+__device__ int wait_state_l(const Args& a, int b)
+{
+    __shared__ int s_code;
+    const unsigned long long t0 = wall_clock64();
+    for (;;) {
+        bool got = false;
+        if (threadIdx.x == 0) {
+            const unsigned long long v = get_u64(&a.sstate[b]);
+            got = f64_ok(v, a.epoch) && !a.force_recompute;
+            s_code = got ? (int)(v >> 8) : 0;
+        }
+        if (__syncthreads_or(got)) break;
+        if (wait_expired(a, t0)) break;
+        __builtin_amdgcn_s_sleep(2);
+    }
+    const int code = s_code;
+    __syncthreads();
+    return code;
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kThreads, 4) void sv_logits_kernel(Args a)
+{
+    const int NC = a.NC, K = a.K, V = a.V;
+    const float kt = a.ktau;
+
+    if (blockIdx.x >= a.nwalk) {
+        // bonus row K (target only), two chunks per block; the block of the
+        // rotating finishing column finishes the sequence
+        const int per_seq = (NC + kBonusChunks - 1) / kBonusChunks;
+        const unsigned blk = blockIdx.x - a.nwalk;
+        const int b = (int)(blk / (unsigned)per_seq);
+        const int c0 = (int)(blk - (unsigned)b * (unsigned)per_seq) * kBonusChunks;
+        const int64_t row0 = (int64_t)b * (K + 1);
+        const Row prow = row_of(a.tp + (row0 + K) * V, V);
+        float4 xp[kBonusChunks][kVecS];
+#pragma unroll
+        for (int j = 0; j < kBonusChunks; ++j)   // chunks past NC read as zeros and are masked
+            load_chunk_keep<VEC, kVecS>(prow, c0 + j < NC ? c0 + j : NC, xp[j],
+                                        blk + kTailBlocks >= gridDim.x - a.nwalk);
+#pragma unroll
+        for (int j = 0; j < kBonusChunks; ++j) {
+            const int cj = c0 + j < NC ? c0 + j : NC;
+            const LStat st = chunk_stats_l<kVecS, false>(xp[j], xp[j], cj, V, kt, j & 1);
+            if (c0 + j < NC) publish_l(a, row0 + K, c0 + j, st, false);
+        }
+        const int fc = finisher_column(b, NC);
+        if (fc < c0 || fc >= c0 + kBonusChunks) return;
+        __builtin_amdgcn_s_setprio(3);
+        const int code = K > 0 ? wait_state_l(a, b) : K + 1;
+        if (code == K + 1) {
+            draw_and_write_l<VEC>(a, b, K, LRow{0.0, 0.0, 0.0f, 0.0f});
+        } else if (code <= 0) {
+            finish_rows_l<VEC>(a, b);
+        }
+        return;
+    }
+
+    // a walk: chunk column c of draft rows 0..K-1 of sequence b (K >= 1)
+    const int b = (int)(blockIdx.x / (unsigned)NC);
+    const int c = (int)(blockIdx.x - (unsigned)b * (unsigned)NC);
+    const float* tb = a.tp + (int64_t)b * (K + 1) * V;
+    const float* db = a.dp + (int64_t)b * K * V;
+    const int64_t row0 = (int64_t)b * (K + 1);
+    int state = kSearching;
+    LRow rn{0.0, 0.0, 0.0f, 0.0f};
+    int tok = -1;
+    float4 xp[kVecS], xq[kVecS], yp[kVecS], yq[kVecS];
+    load_chunk<VEC, kVecS>(row_of(tb, V), c, xp);
+    load_chunk<VEC, kVecS>(row_of(db, V), c, xq);
+
+    auto decide = [&](int j, const PollL& pl) {
+        LRow r;
+        const int rej = poll_decide_l(a, b, j, pl, &r);
+        if (rej < 0) {
+            state = kLost;
+            if (threadIdx.x == 0)
+                for (int q = j; q < K; ++q)
+                    put_u64(&a.wpart[((int64_t)b * K + q) * NC + c], tag_f64(__builtin_nan(""), a.epoch));
+        } else if (rej) {
+            state = j;
+            rn = r;
+            const double w = block_sum(parked_resid_l(r, kt, c, V));
+            if (threadIdx.x == 0) put_u64(&a.wpart[((int64_t)b * K + j) * NC + c], tag_f64(w, a.epoch));
+        }
+    };
+    auto load_next = [&](int i) {
+        const bool more = i + 1 < K;
+        const int64_t off = more ? (int64_t)(i + 1) * V : 0;
+        load_chunk<VEC, kVecS>(row_of(tb + off, more ? V : 0), c, yp);
+        load_chunk<VEC, kVecS>(row_of(db + off, more ? V : 0), c, yq);
+    };
+
+    int i = 0;
+    for (; i < K; ++i) {
+        PollL pl{0ull, 0ull, 0ull, 0ull, 0.0f, 0.0f, 0.0f, 0};
+        const bool pending = i > 0;
+        if (pending) pl = poll_issue_l(a, b, i - 1, tok);
+        if (threadIdx.x == 0) tok = a.dt[(int64_t)b * K + i];
+        __builtin_amdgcn_sched_barrier(0);
+        load_next(i);
+        __builtin_amdgcn_sched_barrier(0);
+        publish_l(a, row0 + i, c, chunk_stats_l<kVecS, true>(xp, xq, c, V, kt, i & 1), true);
+        if (pending) decide(i - 1, pl);
+        if (state == kSearching) park(xp, xq);
+#pragma unroll
+        for (int j = 0; j < kVecS; ++j) {
+            xp[j] = yp[j];
+            xq[j] = yq[j];
+        }
+        if (state != kSearching) {
+            ++i;
+            break;
+        }
+    }
+    for (; i < K; ++i) {
+        load_next(i);
+        __builtin_amdgcn_sched_barrier(0);
+        publish_l(a, row0 + i, c, chunk_stats_l<kVecS, true>(xp, xq, c, V, kt, i & 1), true);
+#pragma unroll
+        for (int j = 0; j < kVecS; ++j) {
+            xp[j] = yp[j];
+            xq[j] = yq[j];
+        }
+    }
+    if (state == kSearching) {
+        decide(K - 1, poll_issue_l(a, b, K - 1, tok));
+        if (state == kSearching) state = K;
+    }
+    if (c != finisher_column(b, NC)) return;
+    __builtin_amdgcn_s_setprio(3);
+    if (state >= 0 && state < K) draw_and_write_l<VEC>(a, b, state, rn);
+    if (threadIdx.x == 0) put_u64(&a.sstate[b], tag_state(state >= 0 ? state + 1 : 0, a.epoch));
+}
+
 __global__ void sv_fill_zero_kernel(uint4* p, size_t n16)
 {
     const uint4 z = make_uint4(0u, 0u, 0u, 0u);
@@ -1591,6 +2352,54 @@ sv_status sv_verify_sample_batched(const float* target_probs, const float* draft
         hipLaunchKernelGGL((sv_sample_kernel<false, true>), grid, block, 0, s, a);
     else
         hipLaunchKernelGGL((sv_sample_kernel<false, false>), grid, block, 0, s, a);
+    return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+sv_status sv_verify_sample_logits_batched(const float* target_logits, const float* draft_logits,
+                                          const int32_t* draft_tokens, const float* uniforms, float temperature,
+                                          int32_t B, int32_t K, int32_t V,
+                                          int32_t* n_accepted, int32_t* next_token,
+                                          void* workspace, size_t workspace_bytes, void* stream)
+{
+    sv_status st = check_sizes(B, K, V);
+    if (st != SV_OK) return st;
+    if (!(std::isfinite(temperature) && temperature > 0.0f)) return SV_ERR_INVALID_ARG;
+    if (B == 0) return SV_OK;   // nothing to verify; pointers are not inspected
+    if (!target_logits || !uniforms || !n_accepted || !next_token ||
+        (K > 0 && (!draft_logits || !draft_tokens)))
+        return SV_ERR_INVALID_ARG;
+    if (!aligned(target_logits, 4) || !aligned(draft_logits, 4) || !aligned(draft_tokens, 4) ||
+        !aligned(uniforms, 4) || !aligned(n_accepted, 4) || !aligned(next_token, 4))
+        return SV_ERR_INVALID_ARG;
+    if (!workspace || !aligned(workspace, 16) || workspace_bytes < sv_workspace_size(B, K, V, 1))
+        return SV_ERR_WORKSPACE;
+    DevInfo d;
+    st = device_info(&d);
+    if (st != SV_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    Args a = make_args(workspace, B, K, V, true);
+    st = next_epoch(workspace, workspace_bytes, s, &a.epoch);
+    if (st != SV_OK) return st;
+    a.tp = target_logits;
+    a.dp = draft_logits;
+    a.dt = draft_tokens;
+    a.u = uniforms;
+    a.n_out = n_accepted;
+    a.next_out = next_token;
+    // exp(x / tau) = exp2(x * log2(e) / tau)
+    a.ktau = (float)(1.4426950408889634 / (double)temperature);
+    const Tuning tu = tuning();
+    a.force_recompute = tu.force_recompute;
+    a.poll_ticks = (unsigned long long)(tu.poll_us * 1e-3 * (double)d.wall_khz);
+    const bool vec = (V % 4 == 0) && aligned(target_logits, 16) && (K == 0 || aligned(draft_logits, 16));
+    const uint64_t per_row = (uint64_t)B * (uint64_t)a.NC;
+    const uint64_t bonus = (uint64_t)B * (uint64_t)((a.NC + kBonusChunks - 1) / kBonusChunks);
+    a.nwalk = (unsigned)(K > 0 ? per_row : 0);
+    const dim3 grid((unsigned)(a.nwalk + bonus)), block(kThreads);
+    if (vec)
+        hipLaunchKernelGGL((sv_logits_kernel<true>), grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL((sv_logits_kernel<false>), grid, block, 0, s, a);
     return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 

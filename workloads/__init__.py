@@ -126,12 +126,18 @@ def _c4_qeqp_set(seed: int, rnd: int, B: int) -> np.ndarray:
 
 
 def gen_sequence(family: str, b: int, B: int, K: int, V: int, seed: int = 0, rnd: int = 0,
-                 out_p: np.ndarray | None = None, out_q: np.ndarray | None = None):
+                 out_p: np.ndarray | None = None, out_q: np.ndarray | None = None, logits: bool = False):
     """Generate sequence b of a batch.
 
     Returns (p [K+1, V] f32, q [K, V] f32 or None, t [K] int32, u [K+1] f32, info).
     If out_p / out_q are given, the rows are written there (and returned).
+    logits=True (families c1, c3): the rows are the f32 logits themselves, not
+    their softmax, and the draft tokens are drawn from the softmax of the
+    stored draft logits (temperature 1); the random draws are those of the
+    probability rows.
     """
+    if logits and family not in ("c1", "c3"):
+        raise ValueError(f"family {family} has no logits form")
     if family not in _FAMILY_ID:
         raise ValueError(f"unknown family {family!r}")
     rng = _rng(seed, family, rnd, b)
@@ -154,10 +160,15 @@ def gen_sequence(family: str, b: int, B: int, K: int, V: int, seed: int = 0, rnd
             qeqp = bool(_c4_qeqp_set(seed, rnd, B)[b])
             info["q_equals_p"] = qeqp
         for i in range(K + 1):
-            logits = scale * rng.standard_normal(V)
-            p[i] = _softmax_f32(logits)
+            z = scale * rng.standard_normal(V)
+            if logits:
+                p[i] = z.astype(np.float32)
+                if i < K:
+                    q[i] = (z + sigma * rng.standard_normal(V)).astype(np.float32)
+                continue
+            p[i] = _softmax_f32(z)
             if i < K:
-                q[i] = _softmax_f32(logits + sigma * rng.standard_normal(V))
+                q[i] = _softmax_f32(z + sigma * rng.standard_normal(V))
         if family == "c4":
             sp = rng.uniform(0.5, 2.0, size=K + 1).astype(np.float32)
             sq = rng.uniform(0.5, 2.0, size=K).astype(np.float32)
@@ -169,7 +180,7 @@ def gen_sequence(family: str, b: int, B: int, K: int, V: int, seed: int = 0, rnd
                 else:
                     q[i] *= sq[i]
         for i in range(K):
-            t[i] = _draw_index(rng, q[i])
+            t[i] = _draw_index(rng, _softmax_f32(q[i]) if logits else q[i])
     elif family == "c2":
         for i in range(K + 1):
             p[i] = _softmax_f32(3.0 * rng.standard_normal(V))
@@ -215,7 +226,7 @@ def gen_sequence(family: str, b: int, B: int, K: int, V: int, seed: int = 0, rnd
 
 
 def make_batch(family: str, B: int, K: int, V: int, seed: int = 0, rnd: int = 0,
-               seqs=None) -> Batch:
+               seqs=None, logits: bool = False) -> Batch:
     """Generate a whole batch (or only the sequences listed in `seqs`, which
     then become rows 0..len(seqs)-1 of the returned arrays)."""
     idx = list(range(B)) if seqs is None else [int(s) for s in seqs]
@@ -227,7 +238,7 @@ def make_batch(family: str, B: int, K: int, V: int, seed: int = 0, rnd: int = 0,
     infos = []
     for j, b in enumerate(idx):
         _, _, t, uu, info = gen_sequence(family, b, B, K, V, seed, rnd,
-                                         out_p=tp[j], out_q=None if dp is None else dp[j])
+                                         out_p=tp[j], out_q=None if dp is None else dp[j], logits=logits)
         dt[j] = t
         u[j] = uu
         infos.append(info)
@@ -251,17 +262,17 @@ def formula_bytes(B: int, K: int, V: int, sampled: bool) -> int:
 
 
 def _gen_one(args):
-    family, b, B, K, V, seed, rnd = args
-    p, q, t, u, info = gen_sequence(family, b, B, K, V, seed, rnd)
+    family, b, B, K, V, seed, rnd, logits = args
+    p, q, t, u, info = gen_sequence(family, b, B, K, V, seed, rnd, logits=logits)
     return b, p, q, t, u, info
 
 
 def iter_sequences(family: str, B: int, K: int, V: int, seed: int = 0, rnd: int = 0,
-                   seqs=None, workers: int = 1):
+                   seqs=None, workers: int = 1, logits: bool = False):
     """Yield (b, p, q, t, u, info) for each requested sequence, in order,
     generating them in `workers` forked processes when workers > 1."""
     idx = list(range(B)) if seqs is None else [int(s) for s in seqs]
-    jobs = [(family, b, B, K, V, seed, rnd) for b in idx]
+    jobs = [(family, b, B, K, V, seed, rnd, logits) for b in idx]
     if workers <= 1 or len(jobs) <= 1:
         for j in jobs:
             yield _gen_one(j)

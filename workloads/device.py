@@ -11,7 +11,7 @@ from . import CONFIGS, iter_sequences, default_workers
 
 def device_batch(family: str, B: int, K: int, V: int, seed: int = 0, rnd: int = 0,
                  device="cuda", workers: int | None = None, sampled: bool = True,
-                 keep_host=None):
+                 keep_host=None, logits: bool = False):
     """Return dict(tp, dp, dt, u) of device tensors plus 'info' (per-sequence
     generator info) and 'sha256' of the host bytes.  keep_host: optional set
     of sequence indices whose host arrays are also returned in 'host'."""
@@ -26,7 +26,7 @@ def device_batch(family: str, B: int, K: int, V: int, seed: int = 0, rnd: int = 
     h = hashlib.sha256()
     pin_p = torch.empty((K + 1, V), dtype=torch.float32, pin_memory=True)
     pin_q = torch.empty((max(K, 1), V), dtype=torch.float32, pin_memory=True)
-    for b, p, q, t, uu, info in iter_sequences(family, B, K, V, seed, rnd, workers=workers):
+    for b, p, q, t, uu, info in iter_sequences(family, B, K, V, seed, rnd, workers=workers, logits=logits):
         pin_p.numpy()[...] = p
         tp[b].copy_(pin_p, non_blocking=False)
         h.update(p.tobytes())
