@@ -2003,8 +2003,7 @@ __global__ __launch_bounds__(kThreads, 4) void sv_logits_kernel(Args a)
     const float kt = a.ktau;
 
     if (blockIdx.x >= a.nwalk) {
-        // bonus row K (target only), two chunks per block; the block of the
-        // rotating finishing column finishes the sequence
+        // bonus row K (target only), two chunks per block
         const int per_seq = (NC + kBonusChunks - 1) / kBonusChunks;
         const unsigned blk = blockIdx.x - a.nwalk;
         const int b = (int)(blk / (unsigned)per_seq);
@@ -2022,16 +2021,7 @@ __global__ __launch_bounds__(kThreads, 4) void sv_logits_kernel(Args a)
             const LStat st = chunk_stats_l<kVecS, false>(xp[j], xp[j], cj, V, kt, j & 1);
             if (c0 + j < NC) publish_l(a, row0 + K, c0 + j, st, false);
         }
-        const int fc = finisher_column(b, NC);
-        if (fc < c0 || fc >= c0 + kBonusChunks) return;
-        __builtin_amdgcn_s_setprio(3);
-        const int code = K > 0 ? wait_state_l(a, b) : K + 1;
-        if (code == K + 1) {
-            draw_and_write_l<VEC>(a, b, K, LRow{0.0, 0.0, 0.0f, 0.0f});
-        } else if (code <= 0) {
-            finish_rows_l<VEC>(a, b);
-        }
-        return;
+        return;   // sv_logits_finish_kernel finishes the sequence
     }
 
     // a walk: chunk column c of draft rows 0..K-1 of sequence b (K >= 1)
@@ -2109,6 +2099,23 @@ __global__ __launch_bounds__(kThreads, 4) void sv_logits_kernel(Args a)
     __builtin_amdgcn_s_setprio(3);
     if (state >= 0 && state < K) draw_and_write_l<VEC>(a, b, state, rn);
     if (threadIdx.x == 0) put_u64(&a.sstate[b], tag_state(state >= 0 ? state + 1 : 0, a.epoch));
+}
+
+// The second launch of the logits path, one block per sequence, after
+// sv_logits_kernel has ended (so every word it reads is there): the bonus
+// draw after full acceptance (or K == 0), and the decisions of a sequence
+// whose walks could not decide.  A launch of its own keeps this rarely taken
+// code out of the walk's register allocation.
+template <bool VEC>
+__global__ __launch_bounds__(kThreads) void sv_logits_finish_kernel(Args a)
+{
+    const int b = (int)blockIdx.x, K = a.K;
+    const int code = K > 0 ? wait_state_l(a, b) : K + 1;
+    if (code == K + 1) {
+        draw_and_write_l<VEC>(a, b, K, LRow{0.0, 0.0, 0.0f, 0.0f});
+    } else if (code <= 0) {
+        finish_rows_l<VEC>(a, b);
+    }
 }
 
 __global__ void sv_fill_zero_kernel(uint4* p, size_t n16)
@@ -2396,10 +2403,13 @@ sv_status sv_verify_sample_logits_batched(const float* target_logits, const floa
     const uint64_t bonus = (uint64_t)B * (uint64_t)((a.NC + kBonusChunks - 1) / kBonusChunks);
     a.nwalk = (unsigned)(K > 0 ? per_row : 0);
     const dim3 grid((unsigned)(a.nwalk + bonus)), block(kThreads);
-    if (vec)
+    if (vec) {
         hipLaunchKernelGGL((sv_logits_kernel<true>), grid, block, 0, s, a);
-    else
+        hipLaunchKernelGGL((sv_logits_finish_kernel<true>), dim3((unsigned)B), block, 0, s, a);
+    } else {
         hipLaunchKernelGGL((sv_logits_kernel<false>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((sv_logits_finish_kernel<false>), dim3((unsigned)B), block, 0, s, a);
+    }
     return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
