@@ -35,7 +35,7 @@ __all__ = [
     "sv_workspace_size", "sv_workspace_init", "sv_workspace_error", "sv_status_string",
     "sv_verify_greedy_batched", "sv_verify_sample_batched", "sv_verify_sample_logits_batched",
     "verify_greedy", "verify_sample", "stats_to_numpy", "workspace_for",
-    "SpeculativeDecoder", "DecodeStats",
+    "SpeculativeDecoder", "DecodeStats", "Governor",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -299,4 +299,4 @@ def verify_sample(target_probs, draft_probs, draft_tokens, uniforms, **kw):
 
 
 # The multi-round driver (the card's SpeculativeDecoder), over the calls above.
-from .decoder import DecodeStats, SpeculativeDecoder  # noqa: E402
+from .decoder import DecodeStats, Governor, SpeculativeDecoder  # noqa: E402

@@ -23,11 +23,28 @@ sequence) and return tokens [b, k], probs [b, k, V] and target_probs
 sequence leaves the batch once it has max_new tokens (or emitted the stop
 token).
 
+Telemetry and the governor follow the SPEL README (section 1.3, the Dynamic
+Speculation Governor, and its definition of the acceptance fraction as
+accepted draft tokens over proposed ones; corrections and bonus tokens are
+delivered output, not accepted drafts).  A Governor, per sequence, keeps the
+accepted/proposed ratio over a window of its last rounds; when that ratio
+falls below alpha_threshold, or a round accepts none of its proposals, the
+sequence stops drafting for the rest of the generate call and continues one
+target token per round (a K = 0 verification: plain greedy or sampled
+target decoding).  It does not resume drafting within the call.
+
+forced_alpha (benchmark only, as the llms-explorer post's forced-acceptance
+ceilings): the drafts and the verification run for real, then the accepted
+prefix is replaced by a run of Bernoulli(forced_alpha) successes drawn from
+the decoder's generator, followed by the argmax of the target row after it.
+The output is then not a decoding of the target.
+
 The verification itself always runs in the library's HIP kernels; `verify`
 replaces it only for tests that exercise this host protocol without a GPU.
 """
 from __future__ import annotations
 
+from collections import deque
 from dataclasses import dataclass, field
 from typing import Callable, List, Optional, Sequence
 
@@ -39,16 +56,68 @@ from . import sv_verify_greedy_batched, sv_verify_sample_batched, workspace_for
 
 @dataclass
 class DecodeStats:
-    """Per-round record of a generate call: rounds run, and for every
-    (round, sequence) the number of drafts accepted."""
+    """Telemetry of a decoder: rounds run; for every drafting (round,
+    sequence) the drafts accepted; per draft position, how often it was
+    tested and accepted; governor trips and the target-only rounds after
+    them."""
     rounds: int = 0
     accepted: List[int] = field(default_factory=list)
+    proposed: int = 0
+    position_tested: np.ndarray = field(default_factory=lambda: np.zeros(0, np.int64))
+    position_accepted: np.ndarray = field(default_factory=lambda: np.zeros(0, np.int64))
+    trips: int = 0
+    ar_rounds: int = 0
+
+    def record(self, k: int, n: int) -> None:
+        if self.position_tested.size < k:
+            grow = k - self.position_tested.size
+            self.position_tested = np.concatenate([self.position_tested, np.zeros(grow, np.int64)])
+            self.position_accepted = np.concatenate([self.position_accepted, np.zeros(grow, np.int64)])
+        self.accepted.append(n)
+        self.proposed += k
+        self.position_tested[:min(n + 1, k)] += 1
+        self.position_accepted[:n] += 1
 
     def mean_accepted(self) -> float:
         return float(np.mean(self.accepted)) if self.accepted else 0.0
 
+    def acceptance_fraction(self) -> float:
+        """Accepted draft tokens over proposed ones."""
+        return float(np.sum(self.accepted)) / self.proposed if self.proposed else 0.0
+
+    def position_rate(self) -> np.ndarray:
+        """Per draft position: accepted over tested."""
+        t = self.position_tested
+        return np.where(t > 0, self.position_accepted / np.maximum(t, 1), 0.0)
+
     def histogram(self, k: int) -> np.ndarray:
         return np.bincount(np.asarray(self.accepted, np.int64), minlength=k + 1)
+
+
+@dataclass
+class Governor:
+    """Stop drafting when the accepted/proposed ratio over the last `window`
+    drafting rounds falls below alpha_threshold, or (trip_on_zero) when a
+    round accepts none of its proposals."""
+    alpha_threshold: float = 0.0
+    window: int = 8
+    trip_on_zero: bool = True
+
+
+class _GovState:
+    def __init__(self, g: Governor):
+        self.g = g
+        self.hist = deque(maxlen=max(1, int(g.window)))
+        self.tripped = False
+
+    def update(self, n: int, k: int) -> bool:
+        """Record a drafting round; True if the governor trips now."""
+        self.hist.append((n, k))
+        acc = sum(a for a, _ in self.hist)
+        prop = sum(p for _, p in self.hist)
+        if (self.g.trip_on_zero and k > 0 and n == 0) or (prop > 0 and acc / prop < self.g.alpha_threshold):
+            self.tripped = True
+        return self.tripped
 
 
 def _as_int32(x, device, shape) -> torch.Tensor:
@@ -69,14 +138,21 @@ class SpeculativeDecoder:
     seed      -- seeds the generator of the sampled rounds' uniforms.
     device    -- device of the verification (default: the current one).
     batched   -- callbacks take and return batches (see the module notes).
+    governor  -- a Governor (per sequence, reset by every generate call).
+    forced_alpha -- benchmark only: force the accepted prefix (see above).
     verify    -- test hook: callable(tp, dp, tokens, uniforms) -> (n, next)
                  on numpy arrays of one round, replacing the library call.
     """
 
     def __init__(self, draft_step: Callable, target_step: Callable, k: int = 4, greedy: bool = True,
-                 seed: int = 0, device=None, batched: bool = False, verify: Optional[Callable] = None):
+                 seed: int = 0, device=None, batched: bool = False, verify: Optional[Callable] = None,
+                 governor: Optional[Governor] = None, forced_alpha: Optional[float] = None):
         if k < 0:
             raise ValueError("k must be >= 0")
+        if forced_alpha is not None and not (0.0 <= forced_alpha <= 1.0):
+            raise ValueError("forced_alpha must lie in [0, 1]")
+        self.governor = governor
+        self.forced_alpha = forced_alpha
         self.draft_step = draft_step
         self.target_step = target_step
         self.k = int(k)
@@ -87,22 +163,32 @@ class SpeculativeDecoder:
         self.rng = np.random.Generator(np.random.PCG64(seed))
         self.stats = DecodeStats()
 
-    # one round for the sequences whose prefixes are given
-    def _round(self, prefixes: List[List[int]]):
-        b, k = len(prefixes), self.k
-        if self.batched:
+    # one round of k proposals (k == 0: target only) for the given prefixes;
+    # returns (tokens [b, k], n [b], next [b], argmax of the target rows
+    # [b, k+1] when forcing, else None)
+    def _round(self, prefixes: List[List[int]], k: int):
+        b = len(prefixes)
+        if k == 0:
+            toks, dprobs = np.zeros((b, 0), np.int32), None
+        elif self.batched:
             toks, dprobs = self.draft_step(prefixes, k)
-            tprobs = self.target_step(prefixes, toks)
         else:
             toks, dprobs = self.draft_step(prefixes[0], k)
-            tprobs = self.target_step(prefixes[0], toks)
+        if self.batched:
+            tprobs = self.target_step(prefixes, toks)
+        else:
+            tprobs = self.target_step(prefixes[0], np.asarray(toks).reshape(-1)[:k] if k else [])
         u = self.rng.random((b, k + 1), dtype=np.float32)
+        forcing = self.forced_alpha is not None and k > 0
         if self.verify is not None:   # test hook: host arrays of the round
             tp = np.asarray(torch.as_tensor(tprobs).cpu(), np.float32).reshape(b, k + 1, -1)
             tk = np.asarray(torch.as_tensor(toks).cpu(), np.int32).reshape(b, k)
-            dp = None if self.greedy else np.asarray(torch.as_tensor(dprobs).cpu(), np.float32).reshape(b, k, -1)
+            V = tp.shape[-1]
+            dp = None if self.greedy else (np.zeros((b, 0, V), np.float32) if k == 0 else
+                                           np.asarray(torch.as_tensor(dprobs).cpu(), np.float32).reshape(b, k, V))
             n, nx = self.verify(tp, dp, tk, u)
-            return np.asarray(tk), np.asarray(n), np.asarray(nx)
+            am = np.argmax(tp, axis=-1) if forcing else None
+            return np.asarray(tk), np.asarray(n), np.asarray(nx), am
         dev = torch.device(self.device) if self.device is not None else torch.device("cuda", torch.cuda.current_device())
         tp = torch.as_tensor(tprobs, device=dev)
         V = tp.shape[-1]
@@ -112,12 +198,18 @@ class SpeculativeDecoder:
         if self.greedy:
             n, nx = sv_verify_greedy_batched(tp, tk, workspace=ws)
         else:
-            dp = _as_f32(dprobs, dev, (b, k, V))
+            dp = (torch.zeros((b, 0, V), dtype=torch.float32, device=dev) if k == 0 else
+                  _as_f32(dprobs, dev, (b, k, V)))
             ut = torch.from_numpy(u).to(dev, non_blocking=False)
             n, nx = sv_verify_sample_batched(tp, dp, tk, ut, workspace=ws)
+        parts = [tk.reshape(-1), n, nx]
+        if forcing:
+            parts.append(torch.argmax(tp, dim=-1).to(torch.int32).reshape(-1))
         # one transfer back (it waits for the round's kernels)
-        host = torch.cat([tk.reshape(-1), n, nx]).cpu().numpy()
-        return host[:b * k].reshape(b, k), host[b * k:b * k + b], host[b * k + b:]
+        host = torch.cat(parts).cpu().numpy()
+        o = b * k
+        am = host[o + 2 * b:].reshape(b, k + 1) if forcing else None
+        return host[:o].reshape(b, k), host[o:o + b], host[o + b:o + 2 * b], am
 
     def generate_many(self, prompts: Sequence[Sequence[int]], max_new: int = 128,
                       stop_token: Optional[int] = None) -> List[List[int]]:
@@ -128,20 +220,37 @@ class SpeculativeDecoder:
         seqs = [list(map(int, p)) for p in prompts]
         new = [0] * len(seqs)
         done = [max_new <= 0] * len(seqs)
+        gov = [_GovState(self.governor) if self.governor is not None else None for _ in seqs]
         while not all(done):
             active = [i for i, d in enumerate(done) if not d]
-            toks, n, nx = self._round([seqs[i] for i in active])
+            drafting = [i for i in active if not (gov[i] and gov[i].tripped)] if self.k > 0 else []
+            plain = [i for i in active if i not in set(drafting)]
             self.stats.rounds += 1
-            for j, i in enumerate(active):
-                nj = int(n[j])
-                self.stats.accepted.append(nj)
-                emitted = [int(t) for t in toks[j, :nj]] + [int(nx[j])]
-                for t in emitted:
-                    seqs[i].append(t)
-                    new[i] += 1
-                    if new[i] >= max_new or (stop_token is not None and t == stop_token):
-                        done[i] = True
-                        break
+            for group, k in ((drafting, self.k), (plain, 0)):
+                if not group:
+                    continue
+                toks, n, nx, am = self._round([seqs[i] for i in group], k)
+                if k == 0 and self.k > 0:
+                    self.stats.ar_rounds += len(group)
+                for j, i in enumerate(group):
+                    nj = int(n[j])
+                    emitted = [int(t) for t in toks[j, :nj]] + [int(nx[j])]
+                    if am is not None:   # forced prefix (benchmark only)
+                        nf = 0
+                        while nf < k and self.rng.random() < self.forced_alpha:
+                            nf += 1
+                        nj = nf
+                        emitted = [int(t) for t in toks[j, :nf]] + [int(am[j, nf])]
+                    if k > 0:
+                        self.stats.record(k, nj)
+                        if gov[i] is not None and not gov[i].tripped and gov[i].update(nj, k):
+                            self.stats.trips += 1
+                    for t in emitted:
+                        seqs[i].append(t)
+                        new[i] += 1
+                        if new[i] >= max_new or (stop_token is not None and t == stop_token):
+                            done[i] = True
+                            break
         return seqs
 
     def generate(self, prompt_ids, max_new: int = 128, stop_token: Optional[int] = None):
