@@ -1367,9 +1367,12 @@ __global__ __launch_bounds__(kThreads, 4) void sv_sample_kernel(Args a)
 // order.  Single weights (p(t), q(t), the residual, the draws) are
 // exp2((l - M) * k) against the same M, on the scale of that mass.
 
+// The argument is one fused multiply-add, l * k - m * k: the rounding of
+// m * k is shared by the whole row, so it scales every weight of the row
+// alike and cancels in the normalised distribution.
 __device__ __forceinline__ float lweight(float l, float m, float k)
 {
-    return __builtin_amdgcn_exp2f((l - m) * k);
+    return __builtin_amdgcn_exp2f(__builtin_fmaf(l, k, -(m * k)));
 }
 
 // Maximum over the wave (all 64 lanes active), the same in every lane.
@@ -1408,19 +1411,20 @@ __device__ __forceinline__ float share_max(const float4 (&v)[NV], int c, int V, 
     return m;
 }
 
-// Sum of the weights of the thread's share against m (fp64; k, then e, ascending).
+// Sum of the weights of the thread's share against m: its 4 * NV weights (at
+// most 1 each) in fp32, k then e ascending, then fp64 from there on.
 template <int NV>
 __device__ __forceinline__ double share_wsum(const float4 (&v)[NV], int c, int V, bool full, float m, float k)
 {
-    double s = 0.0;
+    float s = 0.0f;
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
         const int p0 = 4 * f4_index<NV>(c, j);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            if (full || p0 + e < V) s += (double)lweight(comp(v[j], e), m, k);
+            if (full || p0 + e < V) s += lweight(comp(v[j], e), m, k);
     }
-    return s;
+    return (double)s;
 }
 
 // Block maxima of a and b, in every thread.  Consecutive calls alternate
