@@ -1427,21 +1427,10 @@ __device__ __forceinline__ double share_wsum(const float4 (&v)[NV], int c, int V
     return (double)s;
 }
 
-// Block maxima of a and b, in every thread.  Consecutive calls alternate
-// `slot`, as for block_reduce.
-__device__ __forceinline__ void block_max2(float& a, float& b, int slot)
+// A chunk sum s against maximum m, rescaled to reference M (0 for an empty chunk).
+__device__ __forceinline__ double chunk_scaled(float m, double s, float M, float k)
 {
-    __shared__ float s_a[2][kWaves], s_b[2][kWaves];
-    a = wave_maxf(a);
-    b = wave_maxf(b);
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    if (lane == 0) {
-        s_a[slot][w] = a;
-        s_b[slot][w] = b;
-    }
-    __syncthreads();
-    a = fmaxf(fmaxf(s_a[slot][0], s_a[slot][1]), fmaxf(s_a[slot][2], s_a[slot][3]));
-    b = fmaxf(fmaxf(s_b[slot][0], s_b[slot][1]), fmaxf(s_b[slot][2], s_b[slot][3]));
+    return m == -INFINITY ? 0.0 : s * (double)lweight(m, M, k);
 }
 
 struct LStat {
@@ -1450,20 +1439,50 @@ struct LStat {
 };
 
 // Block-cooperative: (m_c, s_c) of target chunk pv and, with Q, of draft
-// chunk qv.  Consecutive calls alternate `slot`.
+// chunk qv, valid in thread 0.  Each wave sums its weights against its own
+// maximum (found by DPP, no barrier); thread 0 takes the chunk maximum m_c
+// over the four waves and rescales their sums to it, in wave order.
+// Consecutive calls alternate `slot`, as for block_reduce.
 template <int NV, bool Q>
 __device__ __forceinline__ LStat chunk_stats_l(const float4 (&pv)[NV], const float4 (&qv)[NV], int c, int V,
                                                float k, int slot)
 {
+    __shared__ float s_m[2][2][kWaves];
+    __shared__ double s_s[2][2][kWaves];
     const bool full = chunk_full<NV>(c, V);
-    float mp = share_max<NV>(pv, c, V, full);
-    float mq = Q ? share_max<NV>(qv, c, V, full) : -INFINITY;
-    block_max2(mp, mq, slot);
-    Acc t{0.0, 0.0, 0.0, -INFINITY, 0};
-    t.sp = share_wsum<NV>(pv, c, V, full, mp, k);
-    if (Q) t.sq = share_wsum<NV>(qv, c, V, full, mq, k);
-    const Acc r = block_reduce<Q ? (kSP | kSQ) : kSP, false>(t, slot);
-    return LStat{mp, mq, r.sp, r.sq};
+    const float mp = wave_maxf(share_max<NV>(pv, c, V, full));
+    const double sp = wave_sum(share_wsum<NV>(pv, c, V, full, mp, k));
+    float mq = -INFINITY;
+    double sq = 0.0;
+    if (Q) {
+        mq = wave_maxf(share_max<NV>(qv, c, V, full));
+        sq = wave_sum(share_wsum<NV>(qv, c, V, full, mq, k));
+    }
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    if (lane == 0) {
+        s_m[slot][0][w] = mp;
+        s_s[slot][0][w] = sp;
+        s_m[slot][1][w] = mq;
+        s_s[slot][1][w] = sq;
+    }
+    __syncthreads();
+    LStat r{mp, mq, 0.0, 0.0};
+    if (threadIdx.x == 0) {
+        for (int o = 0; o < (Q ? 2 : 1); ++o) {
+            float M = s_m[slot][o][0];
+            for (int j = 1; j < kWaves; ++j) M = fmaxf(M, s_m[slot][o][j]);
+            double S = 0.0;
+            for (int j = 0; j < kWaves; ++j) S += chunk_scaled(s_m[slot][o][j], s_s[slot][o][j], M, k);
+            if (o == 0) {
+                r.mp = M;
+                r.sp = S;
+            } else {
+                r.mq = M;
+                r.sq = S;
+            }
+        }
+    }
+    return r;
 }
 
 // Publish a chunk's (m, s): sums as tagged fp64 words (sp, sq), maxima as
@@ -1485,10 +1504,6 @@ __device__ __forceinline__ void publish_l(const Args& a, int64_t row, int c, con
 // (chunks l and l + 64; m = -inf for none): M is the largest m, the mass is
 // sum_c s_c exp2((m_c - M) k), a lane's pair first, then the fixed wave sum.
 // Every reader of a row uses this.
-__device__ __forceinline__ double chunk_scaled(float m, double s, float M, float k)
-{
-    return m == -INFINITY ? 0.0 : s * (double)lweight(m, M, k);
-}
 __device__ __forceinline__ double row_mass_l(float m0, double s0, float m1, double s1, float k, float* Mout)
 {
     const float M = wave_maxf(fmaxf(m0, m1));
