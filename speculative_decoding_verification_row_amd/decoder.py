@@ -162,6 +162,7 @@ class SpeculativeDecoder:
         self.device = device
         self.rng = np.random.Generator(np.random.PCG64(seed))
         self.stats = DecodeStats()
+        self._bufcache: dict = {}
 
     # one round of k proposals (k == 0: target only) for the given prefixes;
     # returns (tokens [b, k], n [b], next [b], argmax of the target rows
@@ -177,7 +178,7 @@ class SpeculativeDecoder:
         if self.batched:
             tprobs = self.target_step(prefixes, toks)
         else:
-            tprobs = self.target_step(prefixes[0], np.asarray(toks).reshape(-1)[:k] if k else [])
+            tprobs = self.target_step(prefixes[0], toks if k else [])
         u = self.rng.random((b, k + 1), dtype=np.float32)
         forcing = self.forced_alpha is not None and k > 0
         if self.verify is not None:   # test hook: host arrays of the round
@@ -193,23 +194,46 @@ class SpeculativeDecoder:
         tp = torch.as_tensor(tprobs, device=dev)
         V = tp.shape[-1]
         tp = _as_f32(tp, dev, (b, k + 1, V))
+        host_toks = None if isinstance(toks, torch.Tensor) else np.asarray(toks, np.int32).reshape(b, k)
         tk = _as_int32(toks, dev, (b, k))
         ws = workspace_for(b, k, V, not self.greedy, dev)
+        bufs = self._buffers(dev, b, k, forcing)
+        o = b * k
+        dev_out, host_out = bufs["dev"], bufs["host"]
+        n_view, x_view = dev_out[o:o + b], dev_out[o + b:o + 2 * b]
         if self.greedy:
-            n, nx = sv_verify_greedy_batched(tp, tk, workspace=ws)
+            sv_verify_greedy_batched(tp, tk, n_accepted=n_view, next_token=x_view, workspace=ws)
         else:
             dp = (torch.zeros((b, 0, V), dtype=torch.float32, device=dev) if k == 0 else
                   _as_f32(dprobs, dev, (b, k, V)))
-            ut = torch.from_numpy(u).to(dev, non_blocking=False)
-            n, nx = sv_verify_sample_batched(tp, dp, tk, ut, workspace=ws)
-        parts = [tk.reshape(-1), n, nx]
+            bufs["u_pin"].numpy()[...] = u
+            bufs["u_dev"].copy_(bufs["u_pin"], non_blocking=True)
+            sv_verify_sample_batched(tp, dp, tk, bufs["u_dev"], n_accepted=n_view, next_token=x_view, workspace=ws)
+        if host_toks is None:
+            dev_out[:o].copy_(tk.reshape(-1))
         if forcing:
-            parts.append(torch.argmax(tp, dim=-1).to(torch.int32).reshape(-1))
-        # one transfer back (it waits for the round's kernels)
-        host = torch.cat(parts).cpu().numpy()
-        o = b * k
-        am = host[o + 2 * b:].reshape(b, k + 1) if forcing else None
-        return host[:o].reshape(b, k), host[o:o + b], host[o + b:o + 2 * b], am
+            dev_out[o + 2 * b:].copy_(torch.argmax(tp, dim=-1).to(torch.int32).reshape(-1))
+        # one transfer back into pinned memory, then wait for the round's work
+        host_out.copy_(dev_out, non_blocking=True)
+        torch.cuda.current_stream(dev).synchronize()
+        h = host_out.numpy()
+        am = h[o + 2 * b:].reshape(b, k + 1).copy() if forcing else None
+        tks = host_toks if host_toks is not None else h[:o].reshape(b, k).copy()
+        return tks, h[o:o + b].copy(), h[o + b:o + 2 * b].copy(), am
+
+    def _buffers(self, dev, b: int, k: int, forcing: bool) -> dict:
+        """Per (b, k): a device int32 buffer for the round's tokens, n, next
+        (and argmaxes), its pinned host mirror, and pinned/device uniforms."""
+        key = (str(dev), b, k, forcing)
+        bufs = self._bufcache.get(key)
+        if bufs is None:
+            size = b * k + 2 * b + (b * (k + 1) if forcing else 0)
+            bufs = {"dev": torch.empty(size, dtype=torch.int32, device=dev),
+                    "host": torch.empty(size, dtype=torch.int32, pin_memory=True),
+                    "u_pin": torch.empty((b, k + 1), dtype=torch.float32, pin_memory=True),
+                    "u_dev": torch.empty((b, k + 1), dtype=torch.float32, device=dev)}
+            self._bufcache[key] = bufs
+        return bufs
 
     def generate_many(self, prompts: Sequence[Sequence[int]], max_new: int = 128,
                       stop_token: Optional[int] = None) -> List[List[int]]:

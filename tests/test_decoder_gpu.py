@@ -87,3 +87,28 @@ def test_gpu_governed_sampled_law():
     pval, stats = sampled_law_check(None, governor=Governor(alpha_threshold=0.7, window=1))
     assert pval > 1e-4, pval
     assert stats.trips > 1000
+
+
+def test_gpu_device_resident_callbacks():
+    """Callbacks that return device tensors (as a model on the GPU would):
+    the greedy stream still equals plain greedy decoding."""
+    _case("decoder with device-resident callbacks, V=3000")
+    target = HashLM(3000, sigma=2.0, salt=61)
+    draft = HashLM(3000, salt=62, base=target, noise=1.0)
+    ds, ts = make_callbacks(target, draft, greedy=True)
+
+    def ds_dev(prefix, k):
+        t, p = ds(prefix, k)
+        return torch.from_numpy(t).cuda(), torch.from_numpy(p).cuda()
+
+    def ts_dev(prefix, proposed):
+        prop = proposed.cpu().numpy() if isinstance(proposed, torch.Tensor) else proposed
+        return torch.from_numpy(ts(prefix, prop)).cuda()
+
+    for greedy in (True, False):
+        dec = SpeculativeDecoder(ds_dev, ts_dev, k=4, greedy=greedy, seed=5,
+                                 governor=Governor(alpha_threshold=0.0, window=4))
+        out = dec.generate([4, 2], max_new=25)
+        if greedy:
+            assert out == greedy_decode(target, [4, 2], 25)
+        assert len(out) == 27
