@@ -85,7 +85,8 @@ def _random_rows(rng, B, K, V, ties=True, zeros=True):
 # ----------------------------------------------------------- small shapes --
 
 SMALL = [(1, 0, 1), (3, 0, 7), (2, 1, 2), (4, 2, 3), (5, 4, 1000), (3, 3, 1003), (2, 2, 8192),
-         (2, 3, 8193), (2, 2, 16389), (3, 4, 32000), (2, 5, 40001), (1, 2, 65536 + 4)]
+         (2, 3, 8193), (2, 2, 16389), (3, 4, 32000), (2, 5, 40001), (1, 2, 65536 + 4),
+         (3, 9, 5000), (2, 17, 9000)]   # the last two: draft rows in 2 and 3 walk segments
 
 
 # Both kernel variants: with row statistics, and without (the configuration
