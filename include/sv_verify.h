@@ -29,6 +29,10 @@
  * calls made on it (each call tags the words it publishes in the workspace
  * with a number derived from that count); calls that share a workspace must
  * not overlap, so calls on different streams must use different workspaces.
+ * Because that number is chosen on the host when the call is made, a call
+ * must not be captured into a HIP graph that is replayed: every replay would
+ * carry the captured number, and a replay's readers could accept words left
+ * by the one before.
  *
  * Layouts (row-major, V contiguous, f32 = IEEE binary32):
  *   target_probs [B, K+1, V] f32    draft_probs [B, K, V] f32
