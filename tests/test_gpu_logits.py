@@ -99,7 +99,7 @@ def _rows(rng, B, K, V, tau):
 
 
 SMALL = [(1, 0, 1), (3, 0, 7), (2, 1, 2), (4, 2, 3), (5, 4, 1000), (3, 3, 1003), (2, 2, 4096),
-         (2, 3, 4097), (2, 2, 16389), (3, 4, 32000), (2, 5, 40001), (1, 2, 65540)]
+         (2, 3, 4097), (2, 2, 16389), (3, 4, 32000), (2, 5, 40001), (1, 2, 65540), (2, 130, 5000)]
 
 
 @pytest.mark.parametrize("tau", [0.5, 1.0, 2.0])

@@ -86,7 +86,7 @@ def _random_rows(rng, B, K, V, ties=True, zeros=True):
 
 SMALL = [(1, 0, 1), (3, 0, 7), (2, 1, 2), (4, 2, 3), (5, 4, 1000), (3, 3, 1003), (2, 2, 8192),
          (2, 3, 8193), (2, 2, 16389), (3, 4, 32000), (2, 5, 40001), (1, 2, 65536 + 4),
-         (3, 9, 5000), (2, 17, 9000)]   # the last two: draft rows in 2 and 3 walk segments
+         (3, 9, 5000), (2, 17, 9000)]   # the last two: K + 1 rows in 3 and 5 groups of the finishing combine
 
 
 # Both kernel variants: with row statistics, and without (the configuration
@@ -279,6 +279,24 @@ def test_edge_max_vocabulary():
     check_sampled(n, nx, st, oracle.verify_sample(p, q, t, u))
     gn, gx, gst = run_greedy(p, t)
     check_greedy(gn, gx, gst, oracle.verify_greedy(p, t))
+
+
+@pytest.mark.parametrize("B,K,V", [(2, 4096, 5), (2, 257, 9000)], ids=lambda x: str(x))
+def test_edge_max_draft_length(B, K, V):
+    """K = SV_MAX_K draft rows (and a long K over two chunks): one sequence
+    with random rows, one whose drafts are all accepted (q = p, t = argmax,
+    u just below 1), so the bonus draw follows the last of K rows."""
+    _case(f"edge: long draft B={B} K={K} V={V}")
+    rng = np.random.default_rng(K + V)
+    p, q, t, u = _random_rows(rng, B, K, V, ties=True, zeros=True)
+    q[1] = p[1, :K]
+    t[1] = np.argmax(p[1, :K], axis=1)
+    u[1, :K] = np.float32(1) - np.float32(2**-24)
+    os_, og = oracle.verify_sample(p, q, t, u), oracle.verify_greedy(p, t)
+    assert os_["n_accepted"][1] == K and og["n_accepted"][1] == K
+    for stats in STATS:
+        check_sampled(*run_sample(p, q, t, u, stats=stats), os_)
+        check_greedy(*run_greedy(p, t, stats=stats), og)
 
 
 def test_edge_unaligned_rows_use_scalar_path():
