@@ -1396,34 +1396,50 @@ __device__ __forceinline__ bool chunk_full(int c, int V)
     return (int64_t)(c + 1) * (kThreads * NV * 4) <= (int64_t)V;
 }
 
-// Largest logit of the thread's share of chunk c (positions < V); -inf if none.
+// Set the positions of chunk c at or past V to -inf: such a value cannot be
+// a maximum and its weight exp2(-inf) is +0, which leaves every sum as it
+// would be without the position.  Only the ragged last chunk of a row has
+// such positions; the empty asm keeps this on a branch of its own, so a
+// full chunk pays nothing for it.
 template <int NV>
-__device__ __forceinline__ float share_max(const float4 (&v)[NV], int c, int V, bool full)
+__device__ __forceinline__ void mask_tail_l(float4 (&v)[NV], int c, int V)
 {
-    float m = -INFINITY;
+    if (chunk_full<NV>(c, V)) return;
+    asm volatile("");
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
         const int p0 = 4 * f4_index<NV>(c, k);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            if (full || p0 + e < V) m = fmaxf(m, comp(v[k], e));
+        if (p0 >= V) v[k].x = -INFINITY;
+        if (p0 + 1 >= V) v[k].y = -INFINITY;
+        if (p0 + 2 >= V) v[k].z = -INFINITY;
+        if (p0 + 3 >= V) v[k].w = -INFINITY;
     }
+}
+
+// Largest value of the thread's share (-inf if it holds no position < V).
+template <int NV>
+__device__ __forceinline__ float share_max(const float4 (&v)[NV])
+{
+    float m = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < NV; ++k)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) m = fmaxf(m, comp(v[k], e));
     return m;
 }
 
 // Sum of the weights of the thread's share against m: its 4 * NV weights (at
-// most 1 each) in fp32, k then e ascending, then fp64 from there on.
+// most 1 each) in fp32, k then e ascending, then fp64 from there on.  A
+// share whose values are all -inf (m = -inf) sums to 0.
 template <int NV>
-__device__ __forceinline__ double share_wsum(const float4 (&v)[NV], int c, int V, bool full, float m, float k)
+__device__ __forceinline__ double share_wsum(const float4 (&v)[NV], float m, float k)
 {
+    const float nmk = m == -INFINITY ? 0.0f : -(m * k);   // the argument of lweight(l, m, k)
     float s = 0.0f;
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
-        const int p0 = 4 * f4_index<NV>(c, j);
+    for (int j = 0; j < NV; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            if (full || p0 + e < V) s += lweight(comp(v[j], e), m, k);
-    }
+        for (int e = 0; e < 4; ++e) s += __builtin_amdgcn_exp2f(__builtin_fmaf(comp(v[j], e), k, nmk));
     return (double)s;
 }
 
@@ -1444,19 +1460,19 @@ struct LStat {
 // over the four waves and rescales their sums to it, in wave order.
 // Consecutive calls alternate `slot`, as for block_reduce.
 template <int NV, bool Q>
-__device__ __forceinline__ LStat chunk_stats_l(const float4 (&pv)[NV], const float4 (&qv)[NV], int c, int V,
-                                               float k, int slot)
+__device__ __forceinline__ LStat chunk_stats_l(float4 (&pv)[NV], float4 (&qv)[NV], int c, int V, float k, int slot)
 {
     __shared__ float s_m[2][2][kWaves];
     __shared__ double s_s[2][2][kWaves];
-    const bool full = chunk_full<NV>(c, V);
-    const float mp = wave_maxf(share_max<NV>(pv, c, V, full));
-    const double sp = wave_sum(share_wsum<NV>(pv, c, V, full, mp, k));
+    mask_tail_l<NV>(pv, c, V);
+    if (Q) mask_tail_l<NV>(qv, c, V);
+    const float mp = wave_maxf(share_max<NV>(pv));
+    const double sp = wave_sum(share_wsum<NV>(pv, mp, k));
     float mq = -INFINITY;
     double sq = 0.0;
     if (Q) {
-        mq = wave_maxf(share_max<NV>(qv, c, V, full));
-        sq = wave_sum(share_wsum<NV>(qv, c, V, full, mq, k));
+        mq = wave_maxf(share_max<NV>(qv));
+        sq = wave_sum(share_wsum<NV>(qv, mq, k));
     }
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     if (lane == 0) {

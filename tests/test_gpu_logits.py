@@ -131,6 +131,7 @@ def test_logits_full_size(tau):
     _case(f"logits full size B={B} K={K} V={V} tau={tau} (generating)")
     db = device_batch("c3", B, K, V, seed=0, device=DEV, logits=True)
     ws = sv.workspace_for(B, K, V, True, DEV)
+    sv.sv_workspace_init(ws)   # only this call can set the recompute flag
     _case("logits full size: running")
     n, nx = sv.sv_verify_sample_logits_batched(db["tp"], db["dp"], db["dt"], db["u"], tau, workspace=ws)
     torch.cuda.synchronize()
@@ -150,8 +151,13 @@ def test_logits_recompute_path_is_bit_identical(monkeypatch):
     rng = np.random.default_rng(7)
     lp, lq, t, u = _rows(rng, 6, 5, 40000, 0.8)
     ref = run(lp, lq, t, u, 0.8)
+    ws = torch.empty(sv.sv_workspace_size(6, 5, 40000, True), dtype=torch.uint8, device=DEV)
+    sv.sv_workspace_init(ws)
     monkeypatch.setenv("SV_VERIFY_FORCE_RECOMPUTE", "1")
-    got = run(lp, lq, t, u, 0.8)
+    got = run(lp, lq, t, u, 0.8, workspace=ws)
+    monkeypatch.delenv("SV_VERIFY_FORCE_RECOMPUTE")
+    torch.cuda.synchronize()
+    assert _slow_path_flag(ws) == 1
     assert np.array_equal(ref[0], got[0]) and np.array_equal(ref[1], got[1])
     check(*got, verify_sample_logits(lp, lq, t, u, 0.8))
 
