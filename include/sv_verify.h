@@ -135,9 +135,7 @@ sv_status sv_verify_sample_batched(const float* target_probs, const float* draft
  * the same weights.  One pass over the logits: each chunk publishes its
  * maximum and its weight sum against it, and readers rescale to the row's
  * maximum.  No row statistics.  The workspace is that of the sampled call
- * (sv_workspace_size(B, K, V, 1)).  The call makes two launches on
- * `stream`: the pass, then one block per sequence that makes the bonus draw
- * after full acceptance.
+ * (sv_workspace_size(B, K, V, 1)).  One launch on `stream`.
  * Errors: those of the sampled call, and SV_ERR_INVALID_ARG for a temperature
  * that is not finite and > 0. */
 sv_status sv_verify_sample_logits_batched(const float* target_logits, const float* draft_logits,

@@ -1357,12 +1357,12 @@ __global__ __launch_bounds__(kThreads, 4) void sv_sample_kernel(Args a)
 // distribution of a row of logits l is softmax(l / tau); the card asks that
 // target and draft be warped identically, and one tau warps both here.  The
 // work decomposition, the walk and the finishing are those of
-// sv_sample_kernel; what a chunk publishes differs.  A chunk first takes the
-// block-wide maximum m_c of its target values and of its draft values
-// (positions at or past V left out), then sums the weights
-// exp((l - m_c) / tau) = exp2((l - m_c) * k), k = log2(e) / tau, each in
-// fp32, summed in fp64 in the thread order of the probability pass, and
-// publishes (m_c, s_c) per operand.  A reader of a row takes its maximum M
+// sv_sample_kernel; what a chunk publishes differs.  Per operand, a chunk
+// publishes its maximum m_c (positions at or past V left out) and the sum s_c
+// of the weights exp((l - m_c) / tau) = exp2((l - m_c) * k), k = log2(e) /
+// tau: each wave sums its values' weights against its own maximum (per
+// thread in fp32, then across the wave in fp64), and the chunk rescales the
+// four wave sums to m_c in wave order.  A reader of a row takes its maximum M
 // (the largest m_c) and its mass sum_c s_c exp2((m_c - M) * k), in chunk
 // order.  Single weights (p(t), q(t), the residual, the draws) are
 // exp2((l - M) * k) against the same M, on the scale of that mass.
@@ -1457,7 +1457,8 @@ struct LStat {
 // Block-cooperative: (m_c, s_c) of target chunk pv and, with Q, of draft
 // chunk qv, valid in thread 0.  Each wave sums its weights against its own
 // maximum (found by DPP, no barrier); thread 0 takes the chunk maximum m_c
-// over the four waves and rescales their sums to it, in wave order.
+// over the four waves and rescales their sums to it, in wave order.  The
+// positions of pv and qv at or past V are set to -inf (mask_tail_l).
 // Consecutive calls alternate `slot`, as for block_reduce.
 template <int NV, bool Q>
 __device__ __forceinline__ LStat chunk_stats_l(float4 (&pv)[NV], float4 (&qv)[NV], int c, int V, float k, int slot)
@@ -1976,17 +1977,25 @@ __device__ void draw_and_write_l(const Args& a, int b, int n, LRow r)
     __syncthreads();
 }
 
-// Block-cooperative, for a sequence whose walks could not decide: the
-// decisions from the gathered (or recomputed) partials, then the draw.
+// The decision of sequence b taken by its finishing block when the walks
+// could not take it: the accept-prefix length n and the masses of row n.
+struct LDecision {
+    LRow r;
+    int n;
+};
+
+// Block-cooperative, for a sequence whose walks could not decide (rare):
+// the decisions from the gathered (or recomputed) partials, row by row.  Not
+// inlined, so that this rarely taken code stays out of the register
+// allocation of the walks.
 template <bool VEC>
-__device__ void finish_rows_l(const Args& a, int b)
+__device__ __noinline__ LDecision decide_rows_l(const Args& a, int b)
 {
     __shared__ double s_unused[kMaxNC];
     __shared__ int s_rej;
     const int K = a.K, V = a.V;
     const int64_t row0 = (int64_t)b * (K + 1);
-    LRow rn{0.0, 0.0, 0.0f, 0.0f};
-    int n = K;
+    LDecision d{LRow{0.0, 0.0, 0.0f, 0.0f}, K};
     for (int i = 0; i < K; ++i) {
         const LRow r = gather_row_l<VEC, true>(a, b, i, s_unused);
         if (threadIdx.x == 0) {
@@ -2000,12 +2009,12 @@ __device__ void finish_rows_l(const Args& a, int b)
         const int rej = s_rej;
         __syncthreads();
         if (rej) {
-            n = i;
-            rn = r;
+            d.n = i;
+            d.r = r;
             break;
         }
     }
-    draw_and_write_l<VEC>(a, b, n, rn);
+    return d;
 }
 
 // Block-cooperative: the outcome the walks of sequence b published (n + 1,
@@ -2036,12 +2045,18 @@ __global__ __launch_bounds__(kThreads, 4) void sv_logits_kernel(Args a)
 {
     const int NC = a.NC, K = a.K, V = a.V;
     const float kt = a.ktau;
+    // The finishing block of a sequence draws from row dn (with masses dr)
+    // at the end: one draw serves the walk that found a rejection and the
+    // bonus block that finishes a fully accepted (or undecided) sequence.
+    int b, dn = -1;
+    LRow dr{0.0, 0.0, 0.0f, 0.0f};
+    int walk_code = -1;   // set by a finishing walk: n + 1, or 0 if it could not decide
 
     if (blockIdx.x >= a.nwalk) {
         // bonus row K (target only), two chunks per block
         const int per_seq = (NC + kBonusChunks - 1) / kBonusChunks;
         const unsigned blk = blockIdx.x - a.nwalk;
-        const int b = (int)(blk / (unsigned)per_seq);
+        b = (int)(blk / (unsigned)per_seq);
         const int c0 = (int)(blk - (unsigned)b * (unsigned)per_seq) * kBonusChunks;
         const int64_t row0 = (int64_t)b * (K + 1);
         const Row prow = row_of(a.tp + (row0 + K) * V, V);
@@ -2056,11 +2071,28 @@ __global__ __launch_bounds__(kThreads, 4) void sv_logits_kernel(Args a)
             const LStat st = chunk_stats_l<kVecS, false>(xp[j], xp[j], cj, V, kt, j & 1);
             if (c0 + j < NC) publish_l(a, row0 + K, c0 + j, st, false);
         }
-        return;   // sv_logits_finish_kernel finishes the sequence
-    }
-
+        const int fc = finisher_column(b, NC);
+        if (fc < c0 || fc >= c0 + kBonusChunks) return;
+        // the block of the finishing column finishes the sequence once the
+        // walks' outcome is there: after full acceptance (or K == 0) it draws
+        // the bonus token; after a rejection the finishing walk has drawn
+        __builtin_amdgcn_s_setprio(3);
+        const int code = K > 0 ? wait_state_l(a, b) : K + 1;
+        if (code == K + 1) {
+            dn = K;
+        } else if (code <= 0) {
+            // the callee reads the arguments where the kernel received
+            // them, so the kernel keeps no copy of them in scratch memory
+            const Args& ka = *(const Args*)(const void*)__builtin_amdgcn_kernarg_segment_ptr();
+            const LDecision d = decide_rows_l<VEC>(ka, b);
+            dn = d.n;
+            dr = d.r;
+        } else {
+            return;
+        }
+    } else {
     // a walk: chunk column c of draft rows 0..K-1 of sequence b (K >= 1)
-    const int b = (int)(blockIdx.x / (unsigned)NC);
+    b = (int)(blockIdx.x / (unsigned)NC);
     const int c = (int)(blockIdx.x - (unsigned)b * (unsigned)NC);
     const float* tb = a.tp + (int64_t)b * (K + 1) * V;
     const float* db = a.dp + (int64_t)b * K * V;
@@ -2132,25 +2164,16 @@ __global__ __launch_bounds__(kThreads, 4) void sv_logits_kernel(Args a)
     }
     if (c != finisher_column(b, NC)) return;
     __builtin_amdgcn_s_setprio(3);
-    if (state >= 0 && state < K) draw_and_write_l<VEC>(a, b, state, rn);
-    if (threadIdx.x == 0) put_u64(&a.sstate[b], tag_state(state >= 0 ? state + 1 : 0, a.epoch));
-}
-
-// The second launch of the logits path, one block per sequence, after
-// sv_logits_kernel has ended (so every word it reads is there): the bonus
-// draw after full acceptance (or K == 0), and the decisions of a sequence
-// whose walks could not decide.  A launch of its own keeps this rarely taken
-// code out of the walk's register allocation.
-template <bool VEC>
-__global__ __launch_bounds__(kThreads) void sv_logits_finish_kernel(Args a)
-{
-    const int b = (int)blockIdx.x, K = a.K;
-    const int code = K > 0 ? wait_state_l(a, b) : K + 1;
-    if (code == K + 1) {
-        draw_and_write_l<VEC>(a, b, K, LRow{0.0, 0.0, 0.0f, 0.0f});
-    } else if (code <= 0) {
-        finish_rows_l<VEC>(a, b);
+    walk_code = state >= 0 ? state + 1 : 0;
+    if (state >= 0 && state < K) {
+        dn = state;
+        dr = rn;
     }
+    }
+    if (dn >= 0) draw_and_write_l<VEC>(a, b, dn, dr);
+    // the walks' outcome, for the bonus block that finishes the sequence:
+    // n + 1 (the draw is then made when n < K), 0 when they could not decide
+    if (walk_code >= 0 && threadIdx.x == 0) put_u64(&a.sstate[b], tag_state(walk_code, a.epoch));
 }
 
 __global__ void sv_fill_zero_kernel(uint4* p, size_t n16)
@@ -2440,10 +2463,8 @@ sv_status sv_verify_sample_logits_batched(const float* target_logits, const floa
     const dim3 grid((unsigned)(a.nwalk + bonus)), block(kThreads);
     if (vec) {
         hipLaunchKernelGGL((sv_logits_kernel<true>), grid, block, 0, s, a);
-        hipLaunchKernelGGL((sv_logits_finish_kernel<true>), dim3((unsigned)B), block, 0, s, a);
     } else {
         hipLaunchKernelGGL((sv_logits_kernel<false>), grid, block, 0, s, a);
-        hipLaunchKernelGGL((sv_logits_finish_kernel<false>), dim3((unsigned)B), block, 0, s, a);
     }
     return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
