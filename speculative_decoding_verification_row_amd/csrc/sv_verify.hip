@@ -77,6 +77,7 @@ constexpr double kPollMicroseconds = 200.0;     // bound of a wait before recomp
 constexpr int kBonusChunks = 2;                 // bonus-row chunks per block (sampled)
 constexpr unsigned kTailBlocks = 2048;          // the last two waves of 256 CUs x 4 resident blocks
 constexpr int kGreedyWalkRows = 1;              // rows a greedy block walks (one: shortest tail)
+constexpr uint64_t kRowsBlocksPerRow = 512;     // one block per sampled draft row up to 512 * max(4, K) blocks
 
 struct Header {              // 256 bytes
     unsigned error;          // fault word (reserved: nothing in this version sets it)
@@ -1182,7 +1183,7 @@ __device__ __forceinline__ unsigned long long tag_state(int code, unsigned ep)
 
 // Block-cooperative: the finishing step of sequence b, run by the block of
 // its bonus row that finishes it (the last work of the sequence).
-template <bool VEC, bool STATS>
+template <bool VEC, bool STATS, bool ROWS>
 __device__ void finish_bonus(const Args& a, int b)
 {
     constexpr int MP = STATS ? (kSP | kSQ | kSMIN | kAM) : (kSP | kSQ);
@@ -1194,9 +1195,10 @@ __device__ void finish_bonus(const Args& a, int b)
     double Pn = 0.0, Qn = 0.0;
     if (K == 0) {
         n = 0;
-    } else {
+    } else if (!ROWS) {
         // the walks' outcome (published when the walks ended, normally long
-        // before this block runs); without it, decide here from the partials
+        // before this block runs); without it, decide here from the partials,
+        // as always when each draft row has blocks of its own (no outcome)
         const unsigned long long t0 = wall_clock64();
         for (;;) {
             bool got = false;
@@ -1225,7 +1227,7 @@ __device__ void finish_bonus(const Args& a, int b)
     if (!drawn) draw_and_write<VEC, MB>(a, b, n, Pn, Qn);
 }
 
-template <bool VEC, bool STATS>
+template <bool VEC, bool STATS, bool ROWS>
 __global__ __launch_bounds__(kThreads, 4) void sv_sample_kernel(Args a)
 {
     constexpr int MP = STATS ? (kSP | kSQ | kSMIN | kAM) : (kSP | kSQ);   // rows 0..K-1
@@ -1254,7 +1256,35 @@ __global__ __launch_bounds__(kThreads, 4) void sv_sample_kernel(Args a)
         const int fc = finisher_column(b, NC);
         if (fc < c0 || fc >= c0 + kBonusChunks) return;
         __builtin_amdgcn_s_setprio(3);   // latency matters here: the last of these end the kernel
-        finish_bonus<VEC, STATS>(a, b);
+        finish_bonus<VEC, STATS, ROWS>(a, b);
+        return;
+    }
+
+    if constexpr (ROWS) {
+        // One block per (sequence b, draft row i, chunk c), every row at
+        // once: the form for small grids, where a walk's row-after-row
+        // latency would dominate.
+        // The block publishes its partials, decides row i from its siblings'
+        // (the decision every reader takes) and, when row i is rejected,
+        // publishes its chunk's residual mass.  The block that finishes the
+        // bonus row decides the sequence from the partials and draws.
+        const unsigned w = blockIdx.x / (unsigned)NC;
+        const int b = (int)(w / (unsigned)K);
+        const int i = (int)(w - (unsigned)b * (unsigned)K);
+        const int c = (int)(blockIdx.x - w * (unsigned)NC);
+        const int64_t row = (int64_t)b * (K + 1) + i;
+        float4 xp[kVecS], xq[kVecS];
+        load_chunk<VEC, kVecS>(row_of(a.tp + row * V, V), c, xp);
+        load_chunk<VEC, kVecS>(row_of(a.dp + ((int64_t)b * K + i) * V, V), c, xq);
+        const int tok = threadIdx.x == 0 ? a.dt[(int64_t)b * K + i] : -1;
+        publish_part<MP>(a, row, c, block_reduce<MP, false>(thread_stats<MP, kVecS>(xp, xq, c), 0));
+        park(xp, xq);
+        double P, Q;
+        const int rej = poll_decide(a, b, i, poll_issue(a, b, i, tok), &P, &Q);
+        if (rej != 0) {   // rejected: the residual mass; undecided: marked for recomputing
+            const double m = rej > 0 ? block_sum(parked_resid(P, Q)) : __builtin_nan("");
+            if (threadIdx.x == 0) put_u64(&a.wpart[((int64_t)b * K + i) * NC + c], tag_f64(m, a.epoch));
+        }
         return;
     }
 
@@ -2201,6 +2231,7 @@ std::unordered_map<const void*, WsState> g_ws;
 struct Tuning {
     double poll_us = kPollMicroseconds;
     int force_recompute = 0;
+    int rows = -1;           // sampled form: -1 by size, 0 walks, 1 one block per row
 };
 
 // Read at every call: SV_VERIFY_POLL_US bounds a wait for a sibling's
@@ -2211,6 +2242,7 @@ Tuning tuning()
     Tuning r;
     if (const char* s = std::getenv("SV_VERIFY_POLL_US")) r.poll_us = std::atof(s);
     if (const char* s = std::getenv("SV_VERIFY_FORCE_RECOMPUTE")) r.force_recompute = std::atoi(s) != 0;
+    if (const char* s = std::getenv("SV_VERIFY_ROWS")) r.rows = std::atoi(s) != 0 ? 1 : 0;
     if (!(r.poll_us >= 0.0) || r.poll_us > 1e7) r.poll_us = kPollMicroseconds;
     return r;
 }
@@ -2233,6 +2265,15 @@ sv_status device_info(DevInfo* out)
 }
 
 inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+template <bool VEC, bool STATS>
+void launch_sample(bool rows, dim3 grid, hipStream_t s, const Args& a)
+{
+    if (rows)
+        hipLaunchKernelGGL((sv_sample_kernel<VEC, STATS, true>), grid, dim3(kThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL((sv_sample_kernel<VEC, STATS, false>), grid, dim3(kThreads), 0, s, a);
+}
 
 sv_status check_sizes(int32_t B, int32_t K, int32_t V)
 {
@@ -2407,16 +2448,25 @@ sv_status sv_verify_sample_batched(const float* target_probs, const float* draft
     const bool vec = (V % 4 == 0) && aligned(target_probs, 16) && (K == 0 || aligned(draft_probs, 16));
     const uint64_t per_row = (uint64_t)B * (uint64_t)a.NC;
     const uint64_t bonus = (uint64_t)B * (uint64_t)((a.NC + kBonusChunks - 1) / kBonusChunks);
-    a.nwalk = (unsigned)(K > 0 ? per_row : 0);   // the walks, then the bonus-row blocks
-    const dim3 grid((unsigned)(a.nwalk + bonus)), block(kThreads);
+    // One block per draft row for small grids, walks down the rows
+    // otherwise.  A walk's latency grows with its K rows, the row form's with
+    // the waves of blocks it takes to fill the chip (its blocks wait for their
+    // row's siblings), so the limit grows with K: up to 512 * max(4, K)
+    // blocks, where the row form measured faster or equal.  Both forms take
+    // the same decisions from the same words: the outputs do not depend on
+    // the form.
+    bool rows = K > 0 && (uint64_t)K * per_row + bonus <= kRowsBlocksPerRow * (uint64_t)(K > 4 ? K : 4);
+    if (tu.rows >= 0) rows = K > 0 && tu.rows == 1;
+    a.nwalk = (unsigned)(K > 0 ? (rows ? (uint64_t)K * per_row : per_row) : 0);   // then the bonus-row blocks
+    const dim3 grid((unsigned)(a.nwalk + bonus));
     if (vec && stats)
-        hipLaunchKernelGGL((sv_sample_kernel<true, true>), grid, block, 0, s, a);
+        launch_sample<true, true>(rows, grid, s, a);
     else if (vec)
-        hipLaunchKernelGGL((sv_sample_kernel<true, false>), grid, block, 0, s, a);
+        launch_sample<true, false>(rows, grid, s, a);
     else if (stats)
-        hipLaunchKernelGGL((sv_sample_kernel<false, true>), grid, block, 0, s, a);
+        launch_sample<false, true>(rows, grid, s, a);
     else
-        hipLaunchKernelGGL((sv_sample_kernel<false, false>), grid, block, 0, s, a);
+        launch_sample<false, false>(rows, grid, s, a);
     return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 

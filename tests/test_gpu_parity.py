@@ -94,6 +94,15 @@ SMALL = [(1, 0, 1), (3, 0, 7), (2, 1, 2), (4, 2, 3), (5, 4, 1000), (3, 3, 1003),
 STATS = [True, False]
 
 
+# Both forms of the sampled pass: walks down the draft rows, and one block per
+# draft row (which the library picks by itself when every block fits on the
+# chip at once).  SV_VERIFY_ROWS forces one or the other.
+@pytest.fixture(params=["walks", "rows"])
+def form(request, monkeypatch):
+    monkeypatch.setenv("SV_VERIFY_ROWS", "1" if request.param == "rows" else "0")
+    return request.param
+
+
 @pytest.mark.parametrize("stats", STATS, ids=["stats", "nostats"])
 @pytest.mark.parametrize("B,K,V", SMALL, ids=lambda x: str(x))
 def test_greedy_small(B, K, V, stats):
@@ -106,8 +115,8 @@ def test_greedy_small(B, K, V, stats):
 
 @pytest.mark.parametrize("stats", STATS, ids=["stats", "nostats"])
 @pytest.mark.parametrize("B,K,V", SMALL, ids=lambda x: str(x))
-def test_sampled_small(B, K, V, stats):
-    _case(f"sampled small B={B} K={K} V={V} stats={stats}")
+def test_sampled_small(B, K, V, stats, form):
+    _case(f"sampled small B={B} K={K} V={V} stats={stats} form={form}")
     rng = np.random.default_rng(7 + B * 1000 + K * 100 + V)
     p, q, t, u = _random_rows(rng, B, K, V)
     n, nx, st = run_sample(p, q, t, u, stats=stats)
@@ -117,8 +126,8 @@ def test_sampled_small(B, K, V, stats):
 @pytest.mark.parametrize("stats", STATS, ids=["stats", "nostats"])
 @pytest.mark.parametrize("family,B,K,V", [("c1", 16, 4, 32000), ("c3", 24, 5, 24577),
                                           ("c4", 32, 8, 12000), ("c5", 6, 16, 30011)])
-def test_sampled_families_reduced(family, B, K, V, stats):
-    _case(f"sampled {family} B={B} K={K} V={V} stats={stats}")
+def test_sampled_families_reduced(family, B, K, V, stats, form):
+    _case(f"sampled {family} B={B} K={K} V={V} stats={stats} form={form}")
     b = workloads.make_batch(family, B, K, V, seed=5)
     args = (b.target_probs, b.draft_probs, b.draft_tokens, b.uniforms)
     n, nx, st = run_sample(*args, stats=stats)
@@ -211,13 +220,13 @@ def test_workload1_600_rounds_and_law():
 
 # ---------------------------------------------------------- enumeration --
 
-def test_exact_enumeration_cells_on_gpu():
+def test_exact_enumeration_cells_on_gpu(form):
     """Every cell of the tiny-V enumeration (one sequence each) as one batch:
     the GPU must return the oracle's outcome for every cell (cells are far
     from their boundaries)."""
     from test_oracle_law import _cells, _instance
     for K, V, seed in [(0, 8, 1), (1, 5, 3), (2, 6, 6), (3, 8, 8)]:
-        _case(f"enumeration K={K} V={V}")
+        _case(f"enumeration K={K} V={V} form={form}")
         p, q = _instance(np.random.default_rng(1000 + seed), K, V)
         t, u, wts, expect = _cells(p, q)
         B = len(wts)
@@ -242,8 +251,8 @@ def test_edge_empty_batch():
     assert n.numel() == 0
 
 
-def test_edge_out_of_range_tokens_and_one_hot():
-    _case("edge: out-of-range tokens, one-hot rows, q = p")
+def test_edge_out_of_range_tokens_and_one_hot(form):
+    _case(f"edge: out-of-range tokens, one-hot rows, q = p, form={form}")
     rng = np.random.default_rng(11)
     B, K, V = 8, 3, 9000
     p, q, t, u = _random_rows(rng, B, K, V, ties=False)
@@ -285,11 +294,11 @@ def test_edge_max_vocabulary():
 
 
 @pytest.mark.parametrize("B,K,V", [(2, 4096, 5), (2, 257, 9000)], ids=lambda x: str(x))
-def test_edge_max_draft_length(B, K, V):
+def test_edge_max_draft_length(B, K, V, form):
     """K = SV_MAX_K draft rows (and a long K over two chunks): one sequence
     with random rows, one whose drafts are all accepted (q = p, t = argmax,
     u just below 1), so the bonus draw follows the last of K rows."""
-    _case(f"edge: long draft B={B} K={K} V={V}")
+    _case(f"edge: long draft B={B} K={K} V={V} form={form}")
     rng = np.random.default_rng(K + V)
     p, q, t, u = _random_rows(rng, B, K, V, ties=True, zeros=True)
     q[1] = p[1, :K]
@@ -302,10 +311,10 @@ def test_edge_max_draft_length(B, K, V):
         check_greedy(*run_greedy(p, t, stats=stats), og)
 
 
-def test_edge_unaligned_rows_use_scalar_path():
+def test_edge_unaligned_rows_use_scalar_path(form):
     """A base pointer that is 4- but not 16-byte aligned selects the scalar
     load path; results must not change."""
-    _case("edge: unaligned base pointers")
+    _case(f"edge: unaligned base pointers, form={form}")
     rng = np.random.default_rng(13)
     B, K, V = 3, 3, 20000
     p, q, t, u = _random_rows(rng, B, K, V)
@@ -375,11 +384,11 @@ def _slow_path_flag(ws):
 
 @pytest.mark.parametrize("B,K,V", [(6, 5, 40000), (3, 0, 9000), (4, 3, 10001), (2, 9, 70001)],
                          ids=lambda x: str(x))
-def test_recompute_path_is_bit_identical(B, K, V, monkeypatch):
+def test_recompute_path_is_bit_identical(B, K, V, form, monkeypatch):
     """Readers that recompute a sibling's partial (the path taken when a
     sibling has not been scheduled within the wait bound) produce exactly the
     published values: forcing every reader to recompute changes no bit."""
-    _case(f"recompute path B={B} K={K} V={V}")
+    _case(f"recompute path B={B} K={K} V={V} form={form}")
     rng = np.random.default_rng(B * 1000 + K * 10 + V % 7)
     p, q, t, u = _random_rows(rng, B, K, V)
     ref_s = run_sample(p, q, t, u)
