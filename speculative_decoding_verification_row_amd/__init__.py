@@ -113,6 +113,20 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _call(device_index: int, fn, *args):
+    """fn(*args) with `device_index` current (switched only if it is not)."""
+    if torch.cuda.current_device() == device_index:
+        return fn(*args)
+    with torch.cuda.device(device_index):
+        return fn(*args)
+
+
+def _stream_handle(stream, device_index: int) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device_index)
+    return int(stream.cuda_stream)
+
+
 def sv_workspace_init(workspace: torch.Tensor, stream=None) -> None:
     with torch.cuda.device(workspace.device):
         st = load_library().sv_workspace_init(_ptr(workspace), workspace.numel() * workspace.element_size(),
@@ -152,35 +166,52 @@ def workspace_for(B: int, K: int, V: int, sampled: bool, device, stream=None) ->
     return ws
 
 
-def _check(t: torch.Tensor, name: str, dtype, shape, device):
+def _check(t: torch.Tensor, name: str, dtype, shape: tuple, device_index: int):
+    """A contiguous tensor of this dtype and shape on GPU `device_index`: the
+    kernels read and write exactly that many elements from its pointer."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.dtype != dtype:
+    if t.dtype is not dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
-    if tuple(t.shape) != tuple(shape):
-        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
-    if t.device != device or t.device.type != "cuda":
-        raise ValueError(f"{name} must be on {device}")
+    if t.shape != shape:
+        raise ValueError(f"{name} must have shape {shape}, got {tuple(t.shape)}")
+    if not t.is_cuda or t.get_device() != device_index:
+        raise ValueError(f"{name} must be on cuda:{device_index}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
 
 
-def _outputs(B, device, n_accepted, next_token):
+def _device_of(t: torch.Tensor, name: str) -> int:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a tensor on a HIP device")
+    return t.get_device()
+
+
+def _check_workspace(ws: torch.Tensor, device_index: int):
+    """Any contiguous tensor on the call's GPU; its byte size is passed on and
+    the library checks it against sv_workspace_size."""
+    if not isinstance(ws, torch.Tensor) or not ws.is_cuda or ws.get_device() != device_index:
+        raise ValueError(f"workspace must be a tensor on cuda:{device_index}")
+    if not ws.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+
+
+def _outputs(B, device_index, n_accepted, next_token):
     if n_accepted is None:
-        n_accepted = torch.empty(B, dtype=torch.int32, device=device)
+        n_accepted = torch.empty(B, dtype=torch.int32, device=device_index)
     if next_token is None:
-        next_token = torch.empty(B, dtype=torch.int32, device=device)
-    _check(n_accepted, "n_accepted", torch.int32, (B,), device)
-    _check(next_token, "next_token", torch.int32, (B,), device)
+        next_token = torch.empty(B, dtype=torch.int32, device=device_index)
+    _check(n_accepted, "n_accepted", torch.int32, (B,), device_index)
+    _check(next_token, "next_token", torch.int32, (B,), device_index)
     return n_accepted, next_token
 
 
-def _stats_buf(stats, B, K, device):
+def _stats_buf(stats, B, K, device_index):
     if stats is True:
-        stats = torch.empty((B, K + 1, 48), dtype=torch.uint8, device=device)
+        stats = torch.empty((B, K + 1, 48), dtype=torch.uint8, device=device_index)
     if stats is None or stats is False:
         return None
-    _check(stats, "stats", torch.uint8, (B, K + 1, 48), device)
+    _check(stats, "stats", torch.uint8, (B, K + 1, 48), device_index)
     return stats
 
 
@@ -195,18 +226,18 @@ def sv_verify_greedy_batched(target_probs: torch.Tensor, draft_tokens: torch.Ten
     sv_row_stats (see stats_to_numpy)."""
     B, K1, V = target_probs.shape
     K = K1 - 1
-    dev = target_probs.device
+    dev = _device_of(target_probs, "target_probs")
     _check(target_probs, "target_probs", torch.float32, (B, K1, V), dev)
     _check(draft_tokens, "draft_tokens", torch.int32, (B, K), dev)
     n_accepted, next_token = _outputs(B, dev, n_accepted, next_token)
     st = _stats_buf(stats, B, K, dev)
-    with torch.cuda.device(dev):
-        if workspace is None:
-            workspace = workspace_for(B, K, V, False, dev, stream)
-        rc = load_library().sv_verify_greedy_batched(
-            _ptr(target_probs), _ptr(draft_tokens), B, K, V, _ptr(n_accepted), _ptr(next_token),
-            _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(st),
-            _stream_ptr(stream, dev))
+    if workspace is None:
+        workspace = workspace_for(B, K, V, False, dev, stream)
+    _check_workspace(workspace, dev)
+    rc = _call(dev, load_library().sv_verify_greedy_batched,
+               target_probs.data_ptr(), draft_tokens.data_ptr(), B, K, V, n_accepted.data_ptr(),
+               next_token.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+               None if st is None else st.data_ptr(), _stream_handle(stream, dev))
     if rc != SV_OK:
         raise SVError(rc, "sv_verify_greedy_batched")
     return (n_accepted, next_token, st) if st is not None else (n_accepted, next_token)
@@ -223,21 +254,21 @@ def sv_verify_sample_batched(target_probs: torch.Tensor, draft_probs: torch.Tens
     (n_accepted, next_token[, stats]) like sv_verify_greedy_batched."""
     B, K1, V = target_probs.shape
     K = K1 - 1
-    dev = target_probs.device
+    dev = _device_of(target_probs, "target_probs")
     _check(target_probs, "target_probs", torch.float32, (B, K1, V), dev)
     _check(draft_probs, "draft_probs", torch.float32, (B, K, V), dev)
     _check(draft_tokens, "draft_tokens", torch.int32, (B, K), dev)
     _check(uniforms, "uniforms", torch.float32, (B, K1), dev)
     n_accepted, next_token = _outputs(B, dev, n_accepted, next_token)
     st = _stats_buf(stats, B, K, dev)
-    with torch.cuda.device(dev):
-        if workspace is None:
-            workspace = workspace_for(B, K, V, True, dev, stream)
-        rc = load_library().sv_verify_sample_batched(
-            _ptr(target_probs), _ptr(draft_probs), _ptr(draft_tokens), _ptr(uniforms),
-            B, K, V, _ptr(n_accepted), _ptr(next_token),
-            _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(st),
-            _stream_ptr(stream, dev))
+    if workspace is None:
+        workspace = workspace_for(B, K, V, True, dev, stream)
+    _check_workspace(workspace, dev)
+    rc = _call(dev, load_library().sv_verify_sample_batched,
+               target_probs.data_ptr(), draft_probs.data_ptr(), draft_tokens.data_ptr(), uniforms.data_ptr(),
+               B, K, V, n_accepted.data_ptr(), next_token.data_ptr(),
+               workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+               None if st is None else st.data_ptr(), _stream_handle(stream, dev))
     if rc != SV_OK:
         raise SVError(rc, "sv_verify_sample_batched")
     return (n_accepted, next_token, st) if st is not None else (n_accepted, next_token)
@@ -254,19 +285,19 @@ def sv_verify_sample_logits_batched(target_logits: torch.Tensor, draft_logits: t
     (n_accepted, next_token)."""
     B, K1, V = target_logits.shape
     K = K1 - 1
-    dev = target_logits.device
+    dev = _device_of(target_logits, "target_logits")
     _check(target_logits, "target_logits", torch.float32, (B, K1, V), dev)
     _check(draft_logits, "draft_logits", torch.float32, (B, K, V), dev)
     _check(draft_tokens, "draft_tokens", torch.int32, (B, K), dev)
     _check(uniforms, "uniforms", torch.float32, (B, K1), dev)
     n_accepted, next_token = _outputs(B, dev, n_accepted, next_token)
-    with torch.cuda.device(dev):
-        if workspace is None:
-            workspace = workspace_for(B, K, V, True, dev, stream)
-        rc = load_library().sv_verify_sample_logits_batched(
-            _ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens), _ptr(uniforms),
-            ctypes.c_float(float(temperature)), B, K, V, _ptr(n_accepted), _ptr(next_token),
-            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream_ptr(stream, dev))
+    if workspace is None:
+        workspace = workspace_for(B, K, V, True, dev, stream)
+    _check_workspace(workspace, dev)
+    rc = _call(dev, load_library().sv_verify_sample_logits_batched,
+               target_logits.data_ptr(), draft_logits.data_ptr(), draft_tokens.data_ptr(), uniforms.data_ptr(),
+               float(temperature), B, K, V, n_accepted.data_ptr(), next_token.data_ptr(),
+               workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream_handle(stream, dev))
     if rc != SV_OK:
         raise SVError(rc, "sv_verify_sample_logits_batched")
     return n_accepted, next_token
