@@ -78,6 +78,7 @@ constexpr int kBonusChunks = 2;                 // bonus-row chunks per block (s
 constexpr unsigned kTailBlocks = 2048;          // the last two waves of 256 CUs x 4 resident blocks
 constexpr int kGreedyWalkRows = 1;              // rows a greedy block walks (one: shortest tail)
 constexpr uint64_t kRowsBlocksPerRow = 512;     // one block per sampled draft row up to 512 * max(4, K) blocks
+constexpr uint64_t kRowsBlocksPerRowL = 256;    // the same for logits: 256 * max(4, K)
 
 struct Header {              // 256 bytes
     unsigned error;          // fault word (reserved: nothing in this version sets it)
@@ -2070,7 +2071,7 @@ __device__ int wait_state_l(const Args& a, int b)
     return code;
 }
 
-template <bool VEC>
+template <bool VEC, bool ROWS>
 __global__ __launch_bounds__(kThreads, 4) void sv_logits_kernel(Args a)
 {
     const int NC = a.NC, K = a.K, V = a.V;
@@ -2105,9 +2106,10 @@ __global__ __launch_bounds__(kThreads, 4) void sv_logits_kernel(Args a)
         if (fc < c0 || fc >= c0 + kBonusChunks) return;
         // the block of the finishing column finishes the sequence once the
         // walks' outcome is there: after full acceptance (or K == 0) it draws
-        // the bonus token; after a rejection the finishing walk has drawn
+        // the bonus token; after a rejection the finishing walk has drawn.
+        // Row blocks publish no outcome: this block then decides itself.
         __builtin_amdgcn_s_setprio(3);
-        const int code = K > 0 ? wait_state_l(a, b) : K + 1;
+        const int code = K == 0 ? K + 1 : ROWS ? 0 : wait_state_l(a, b);
         if (code == K + 1) {
             dn = K;
         } else if (code <= 0) {
@@ -2120,6 +2122,27 @@ __global__ __launch_bounds__(kThreads, 4) void sv_logits_kernel(Args a)
         } else {
             return;
         }
+    } else if (ROWS) {
+        // one block per (sequence b, draft row i, chunk c), as in the row
+        // form of sv_sample_kernel
+        const unsigned w = blockIdx.x / (unsigned)NC;
+        b = (int)(w / (unsigned)K);
+        const int i = (int)(w - (unsigned)b * (unsigned)K);
+        const int c = (int)(blockIdx.x - w * (unsigned)NC);
+        const int64_t row = (int64_t)b * (K + 1) + i;
+        float4 xp[kVecS], xq[kVecS];
+        load_chunk<VEC, kVecS>(row_of(a.tp + row * V, V), c, xp);
+        load_chunk<VEC, kVecS>(row_of(a.dp + ((int64_t)b * K + i) * V, V), c, xq);
+        const int tok = threadIdx.x == 0 ? a.dt[(int64_t)b * K + i] : -1;
+        publish_l(a, row, c, chunk_stats_l<kVecS, true>(xp, xq, c, V, kt, 0), true);
+        park(xp, xq);
+        LRow r;
+        const int rej = poll_decide_l(a, b, i, poll_issue_l(a, b, i, tok), &r);
+        if (rej != 0) {   // rejected: the residual mass; undecided: marked for recomputing
+            const double m = rej > 0 ? block_sum(parked_resid_l(r, kt, c, V)) : __builtin_nan("");
+            if (threadIdx.x == 0) put_u64(&a.wpart[((int64_t)b * K + i) * NC + c], tag_f64(m, a.epoch));
+        }
+        return;
     } else {
     // a walk: chunk column c of draft rows 0..K-1 of sequence b (K >= 1)
     b = (int)(blockIdx.x / (unsigned)NC);
@@ -2265,6 +2288,22 @@ sv_status device_info(DevInfo* out)
 }
 
 inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// The form of a sampled pass: one block per draft row for small grids, walks
+// down the rows otherwise.  A walk's latency grows with its K rows, the row
+// form's with the waves of blocks it takes to fill the chip (its blocks wait
+// for their row's siblings), so the limit grows with K: up to
+// per_draft_row * max(4, K) blocks, where the row form measured faster or
+// equal (512 on probabilities; 256 on logits, where every rejected row, not
+// only the first, pays a residual of two exp2 per value).  Both forms take
+// the same decisions from the same words: the outputs do not depend on the
+// form.  SV_VERIFY_ROWS forces one (a test hook).
+bool use_rows(int K, uint64_t per_row, uint64_t bonus, uint64_t per_draft_row, const Tuning& tu)
+{
+    if (K <= 0) return false;
+    if (tu.rows >= 0) return tu.rows == 1;
+    return (uint64_t)K * per_row + bonus <= per_draft_row * (uint64_t)(K > 4 ? K : 4);
+}
 
 template <bool VEC, bool STATS>
 void launch_sample(bool rows, dim3 grid, hipStream_t s, const Args& a)
@@ -2448,15 +2487,7 @@ sv_status sv_verify_sample_batched(const float* target_probs, const float* draft
     const bool vec = (V % 4 == 0) && aligned(target_probs, 16) && (K == 0 || aligned(draft_probs, 16));
     const uint64_t per_row = (uint64_t)B * (uint64_t)a.NC;
     const uint64_t bonus = (uint64_t)B * (uint64_t)((a.NC + kBonusChunks - 1) / kBonusChunks);
-    // One block per draft row for small grids, walks down the rows
-    // otherwise.  A walk's latency grows with its K rows, the row form's with
-    // the waves of blocks it takes to fill the chip (its blocks wait for their
-    // row's siblings), so the limit grows with K: up to 512 * max(4, K)
-    // blocks, where the row form measured faster or equal.  Both forms take
-    // the same decisions from the same words: the outputs do not depend on
-    // the form.
-    bool rows = K > 0 && (uint64_t)K * per_row + bonus <= kRowsBlocksPerRow * (uint64_t)(K > 4 ? K : 4);
-    if (tu.rows >= 0) rows = K > 0 && tu.rows == 1;
+    const bool rows = use_rows(K, per_row, bonus, kRowsBlocksPerRow, tu);
     a.nwalk = (unsigned)(K > 0 ? (rows ? (uint64_t)K * per_row : per_row) : 0);   // then the bonus-row blocks
     const dim3 grid((unsigned)(a.nwalk + bonus));
     if (vec && stats)
@@ -2509,13 +2540,17 @@ sv_status sv_verify_sample_logits_batched(const float* target_logits, const floa
     const bool vec = (V % 4 == 0) && aligned(target_logits, 16) && (K == 0 || aligned(draft_logits, 16));
     const uint64_t per_row = (uint64_t)B * (uint64_t)a.NC;
     const uint64_t bonus = (uint64_t)B * (uint64_t)((a.NC + kBonusChunks - 1) / kBonusChunks);
-    a.nwalk = (unsigned)(K > 0 ? per_row : 0);
+    const bool rows = use_rows(K, per_row, bonus, kRowsBlocksPerRowL, tu);
+    a.nwalk = (unsigned)(K > 0 ? (rows ? (uint64_t)K * per_row : per_row) : 0);
     const dim3 grid((unsigned)(a.nwalk + bonus)), block(kThreads);
-    if (vec) {
-        hipLaunchKernelGGL((sv_logits_kernel<true>), grid, block, 0, s, a);
-    } else {
-        hipLaunchKernelGGL((sv_logits_kernel<false>), grid, block, 0, s, a);
-    }
+    if (vec && rows)
+        hipLaunchKernelGGL((sv_logits_kernel<true, true>), grid, block, 0, s, a);
+    else if (vec)
+        hipLaunchKernelGGL((sv_logits_kernel<true, false>), grid, block, 0, s, a);
+    else if (rows)
+        hipLaunchKernelGGL((sv_logits_kernel<false, true>), grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL((sv_logits_kernel<false, false>), grid, block, 0, s, a);
     return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 

@@ -36,6 +36,14 @@ def _need_gpu():
     torch.cuda.synchronize()
 
 
+# Both forms of the pass (walks down the draft rows, one block per draft
+# row); SV_VERIFY_ROWS forces one, the library otherwise picks by size.
+@pytest.fixture(params=["walks", "rows"])
+def form(request, monkeypatch):
+    monkeypatch.setenv("SV_VERIFY_ROWS", "1" if request.param == "rows" else "0")
+    return request.param
+
+
 def _boundary(d):
     return (d["accept_margin"] <= BAND) | (d["draw_margin"] <= BAND) | (d["draw_kind"] >= 4)
 
@@ -104,8 +112,8 @@ SMALL = [(1, 0, 1), (3, 0, 7), (2, 1, 2), (4, 2, 3), (5, 4, 1000), (3, 3, 1003),
 
 @pytest.mark.parametrize("tau", [0.5, 1.0, 2.0])
 @pytest.mark.parametrize("B,K,V", SMALL, ids=lambda x: str(x))
-def test_logits_small(B, K, V, tau):
-    _case(f"logits small B={B} K={K} V={V} tau={tau}")
+def test_logits_small(B, K, V, tau, form):
+    _case(f"logits small B={B} K={K} V={V} tau={tau} form={form}")
     rng = np.random.default_rng(B * 1000 + K * 100 + V + int(tau * 10))
     lp, lq, t, u = _rows(rng, B, K, V, tau)
     o = verify_sample_logits(lp, lq, t, u, tau)
@@ -113,9 +121,9 @@ def test_logits_small(B, K, V, tau):
     check(*run(lp, lq, t, u, tau, offset=True), o)
 
 
-def test_logits_max_vocabulary():
+def test_logits_max_vocabulary(form):
     """V = 524288: 128 chunks per row (wave 0's lanes hold two chunks each)."""
-    _case("logits V=524288 B=2 K=3")
+    _case(f"logits V=524288 B=2 K=3 form={form}")
     rng = np.random.default_rng(99)
     lp, lq, t, u = _rows(rng, 2, 3, 524288, 1.0)
     check(*run(lp, lq, t, u, 1.0), verify_sample_logits(lp, lq, t, u, 1.0))
@@ -146,8 +154,8 @@ def test_logits_full_size(tau):
     assert 0 < n.mean() < K
 
 
-def test_logits_recompute_path_is_bit_identical(monkeypatch):
-    _case("logits forced recompute B=6 K=5 V=40000")
+def test_logits_recompute_path_is_bit_identical(form, monkeypatch):
+    _case(f"logits forced recompute B=6 K=5 V=40000 form={form}")
     rng = np.random.default_rng(7)
     lp, lq, t, u = _rows(rng, 6, 5, 40000, 0.8)
     ref = run(lp, lq, t, u, 0.8)
