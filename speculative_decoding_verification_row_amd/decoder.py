@@ -190,48 +190,63 @@ class SpeculativeDecoder:
             n, nx = self.verify(tp, dp, tk, u)
             am = np.argmax(tp, axis=-1) if forcing else None
             return np.asarray(tk), np.asarray(n), np.asarray(nx), am
-        dev = torch.device(self.device) if self.device is not None else torch.device("cuda", torch.cuda.current_device())
+        dev = self._device()
         tp = torch.as_tensor(tprobs, device=dev)
         V = tp.shape[-1]
         tp = _as_f32(tp, dev, (b, k + 1, V))
         host_toks = None if isinstance(toks, torch.Tensor) else np.asarray(toks, np.int32).reshape(b, k)
         tk = _as_int32(toks, dev, (b, k))
-        ws = workspace_for(b, k, V, not self.greedy, dev)
-        bufs = self._buffers(dev, b, k, forcing)
+        bufs = self._buffers(dev, b, k, V, forcing)
+        stream, ws = bufs["stream"], bufs["ws"]
         o = b * k
         dev_out, host_out = bufs["dev"], bufs["host"]
-        n_view, x_view = dev_out[o:o + b], dev_out[o + b:o + 2 * b]
         if self.greedy:
-            sv_verify_greedy_batched(tp, tk, n_accepted=n_view, next_token=x_view, workspace=ws)
+            sv_verify_greedy_batched(tp, tk, n_accepted=bufs["n"], next_token=bufs["x"], workspace=ws,
+                                     stream=stream)
         else:
             dp = (torch.zeros((b, 0, V), dtype=torch.float32, device=dev) if k == 0 else
                   _as_f32(dprobs, dev, (b, k, V)))
-            bufs["u_pin"].numpy()[...] = u
+            bufs["u_host"][...] = u
             bufs["u_dev"].copy_(bufs["u_pin"], non_blocking=True)
-            sv_verify_sample_batched(tp, dp, tk, bufs["u_dev"], n_accepted=n_view, next_token=x_view, workspace=ws)
+            sv_verify_sample_batched(tp, dp, tk, bufs["u_dev"], n_accepted=bufs["n"], next_token=bufs["x"],
+                                     workspace=ws, stream=stream)
         if host_toks is None:
             dev_out[:o].copy_(tk.reshape(-1))
         if forcing:
             dev_out[o + 2 * b:].copy_(torch.argmax(tp, dim=-1).to(torch.int32).reshape(-1))
         # one transfer back into pinned memory, then wait for the round's work
         host_out.copy_(dev_out, non_blocking=True)
-        torch.cuda.current_stream(dev).synchronize()
-        h = host_out.numpy()
+        stream.synchronize()
+        h = bufs["host_np"]
         am = h[o + 2 * b:].reshape(b, k + 1).copy() if forcing else None
         tks = host_toks if host_toks is not None else h[:o].reshape(b, k).copy()
         return tks, h[o:o + b].copy(), h[o + b:o + 2 * b].copy(), am
 
-    def _buffers(self, dev, b: int, k: int, forcing: bool) -> dict:
-        """Per (b, k): a device int32 buffer for the round's tokens, n, next
-        (and argmaxes), its pinned host mirror, and pinned/device uniforms."""
-        key = (str(dev), b, k, forcing)
+    def _device(self) -> torch.device:
+        if self.device is not None:
+            return torch.device(self.device)
+        return torch.device("cuda", torch.cuda.current_device())
+
+    def _buffers(self, dev, b: int, k: int, V: int, forcing: bool) -> dict:
+        """Per (device, stream, b, k, V): a device int32 buffer for the
+        round's tokens, n, next (and argmaxes) with views of n and next, its
+        pinned host mirror, pinned and device uniforms, the stream and the
+        verification workspace."""
+        stream = torch.cuda.current_stream(dev)
+        key = (dev.index, stream.cuda_stream, b, k, V, forcing)
         bufs = self._bufcache.get(key)
         if bufs is None:
             size = b * k + 2 * b + (b * (k + 1) if forcing else 0)
+            o = b * k
             bufs = {"dev": torch.empty(size, dtype=torch.int32, device=dev),
                     "host": torch.empty(size, dtype=torch.int32, pin_memory=True),
                     "u_pin": torch.empty((b, k + 1), dtype=torch.float32, pin_memory=True),
-                    "u_dev": torch.empty((b, k + 1), dtype=torch.float32, device=dev)}
+                    "u_dev": torch.empty((b, k + 1), dtype=torch.float32, device=dev),
+                    "stream": stream,
+                    "ws": workspace_for(b, k, V, not self.greedy, dev, stream)}
+            bufs["n"], bufs["x"] = bufs["dev"][o:o + b], bufs["dev"][o + b:o + 2 * b]
+            bufs["host_np"] = bufs["host"].numpy()
+            bufs["u_host"] = bufs["u_pin"].numpy()
             self._bufcache[key] = bufs
         return bufs
 
