@@ -1185,7 +1185,7 @@ __device__ __forceinline__ unsigned long long tag_state(int code, unsigned ep)
 // Block-cooperative: the finishing step of sequence b, run by the block of
 // its bonus row that finishes it (the last work of the sequence).
 template <bool VEC, bool STATS, bool ROWS>
-__device__ void finish_bonus(const Args& a, int b)
+__device__ __forceinline__ void finish_bonus(const Args& a, int b)
 {
     constexpr int MP = STATS ? (kSP | kSQ | kSMIN | kAM) : (kSP | kSQ);
     constexpr int MB = STATS ? (kSP | kAM) : kSP;
@@ -1228,6 +1228,15 @@ __device__ void finish_bonus(const Args& a, int b)
     if (!drawn) draw_and_write<VEC, MB>(a, b, n, Pn, Qn);
 }
 
+// The same, not inlined: with row statistics the combine of every row adds
+// enough code that, inlined, it would push the walk loop into spilling.  The
+// callee reads the arguments where the kernel received them.
+template <bool VEC, bool STATS, bool ROWS>
+__device__ __noinline__ void finish_bonus_call(const Args& a, int b)
+{
+    finish_bonus<VEC, STATS, ROWS>(a, b);
+}
+
 template <bool VEC, bool STATS, bool ROWS>
 __global__ __launch_bounds__(kThreads, 4) void sv_sample_kernel(Args a)
 {
@@ -1257,7 +1266,10 @@ __global__ __launch_bounds__(kThreads, 4) void sv_sample_kernel(Args a)
         const int fc = finisher_column(b, NC);
         if (fc < c0 || fc >= c0 + kBonusChunks) return;
         __builtin_amdgcn_s_setprio(3);   // latency matters here: the last of these end the kernel
-        finish_bonus<VEC, STATS, ROWS>(a, b);
+        if constexpr (STATS)
+            finish_bonus_call<VEC, STATS, ROWS>(*(const Args*)(const void*)__builtin_amdgcn_kernarg_segment_ptr(), b);
+        else
+            finish_bonus<VEC, STATS, ROWS>(a, b);
         return;
     }
 
