@@ -445,6 +445,14 @@ def test_binding_and_abi_errors():
         sv.sv_verify_greedy_batched(tp, dt[:, :1].contiguous())
     with pytest.raises(ValueError):
         sv.sv_verify_greedy_batched(tp.cpu(), dt)
+    with pytest.raises(ValueError):   # a strided view: the kernels read rows by pointer
+        sv.sv_verify_greedy_batched(torch.rand((2, 3, 200), device=DEV)[:, :, ::2], dt)
+    with pytest.raises(ValueError):
+        sv.sv_verify_greedy_batched(tp, dt, workspace=torch.zeros(1 << 20, dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        sv.sv_verify_greedy_batched(tp, dt, n_accepted=torch.zeros(3, dtype=torch.int32, device=DEV))
+    with pytest.raises(TypeError):
+        sv.sv_verify_sample_batched(tp, tp[:, :2].contiguous(), dt, torch.rand((2, 3), device=DEV).double())
     small = torch.zeros(16, dtype=torch.uint8, device=DEV)
     with pytest.raises(sv.SVError) as e:
         sv.sv_verify_greedy_batched(tp, dt, workspace=small)
