@@ -149,18 +149,26 @@ def sv_workspace_error(workspace: torch.Tensor, stream=None) -> int:
 _WS: dict = {}
 
 
+_WS_BYTES: dict = {}
+
+
 def workspace_for(B: int, K: int, V: int, sampled: bool, device, stream=None) -> torch.Tensor:
     """An initialised workspace for (device, stream), grown on demand.  One
     workspace per stream: calls on different streams must not share one."""
-    device = torch.device(device)
-    if device.index is None:
-        device = torch.device(device.type, torch.cuda.current_device())
-    s = stream if stream is not None else torch.cuda.current_stream(device)
-    key = (device.index, int(s.cuda_stream))
-    need = max(sv_workspace_size(B, K, V, sampled), 256)
+    if isinstance(device, int):
+        index = device
+    else:
+        device = torch.device(device)
+        index = device.index if device.index is not None else torch.cuda.current_device()
+    s = stream if stream is not None else torch.cuda.current_stream(index)
+    key = (index, s.cuda_stream)
+    shape = (B, K, V, bool(sampled))
+    need = _WS_BYTES.get(shape)
+    if need is None:
+        need = _WS_BYTES[shape] = max(sv_workspace_size(B, K, V, sampled), 256)
     ws = _WS.get(key)
     if ws is None or ws.numel() < need:
-        ws = torch.empty(need, dtype=torch.uint8, device=device)
+        ws = torch.empty(need, dtype=torch.uint8, device=index)
         sv_workspace_init(ws, s)
         _WS[key] = ws
     return ws
