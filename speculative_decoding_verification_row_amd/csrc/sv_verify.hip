@@ -76,7 +76,8 @@ constexpr unsigned kEpochs = 255;               // tags 1..255; 0 marks a cleare
 constexpr double kPollMicroseconds = 200.0;     // bound of a wait before recomputing
 constexpr int kBonusChunks = 2;                 // bonus-row chunks per block (sampled)
 constexpr unsigned kTailBlocks = 2048;          // the last two waves of 256 CUs x 4 resident blocks
-constexpr int kGreedyWalkRows = 1;              // rows a greedy block walks (one: shortest tail)
+constexpr unsigned kGreedyLdsPerBlock = 36864;   // 4 greedy blocks per CU (160 KB of LDS)
+constexpr unsigned kGreedyUncappedBlocks = 2048; // 256 CUs x 8 greedy blocks: smaller grids stay uncapped
 constexpr uint64_t kRowsBlocksPerRow = 512;     // one block per sampled draft row up to 512 * max(4, K) blocks
 constexpr uint64_t kRowsBlocksPerRowL = 256;    // the same for logits: 256 * max(4, K)
 
@@ -127,7 +128,6 @@ struct Args {
     int B, K, V, NC;
     unsigned epoch;                  // this call's tag, 1..255
     int force_recompute;             // test hook: readers recompute every partial
-    int walk_rows;                   // greedy: rows per walk
     unsigned long long poll_ticks;   // wait bound in wall-clock ticks
     float ktau;                      // logits: log2(e) / temperature
 };
@@ -914,27 +914,18 @@ template <bool VEC, bool STATS>
 __global__ __launch_bounds__(kThreads) void sv_greedy_kernel(Args a)
 {
     constexpr int M = STATS ? (kSP | kAM) : kAM;
-    const int NC = a.NC, K = a.K, V = a.V, L = a.walk_rows;
-    const int S = (K + L) / L;                        // walks per column: ceil((K + 1) / L)
-    const unsigned w = blockIdx.x / (unsigned)NC;     // (sequence, segment)
-    const int b = (int)(w / (unsigned)S);
-    const int seg = (int)(w - (unsigned)b * (unsigned)S);
+    const int NC = a.NC, K = a.K, V = a.V;
+    // one block per (sequence b, row r, chunk c): the shortest blocks, so
+    // the grid ends without a long tail
+    const unsigned w = blockIdx.x / (unsigned)NC;
+    const int b = (int)(w / (unsigned)(K + 1));
+    const int r = (int)(w - (unsigned)b * (unsigned)(K + 1));
     const int c = (int)(blockIdx.x - w * (unsigned)NC);
-    const float* tb = a.tp + (int64_t)b * (K + 1) * V;
-    const int64_t row0 = (int64_t)b * (K + 1);
-    const int r0 = seg * L, r1 = (r0 + L < K + 1) ? r0 + L : K + 1;
-
-    // walk rows r0..r1-1 of chunk column c; row i+1 loads while row i reduces
-    float4 x0[kVecG], x1[kVecG];
-    load_chunk<VEC, kVecG>(row_of(tb + (int64_t)r0 * V, V), c, x0);
-    for (int i = r0; i < r1; i += 2) {
-        if (i + 1 < r1) load_chunk<VEC, kVecG>(row_of(tb + (int64_t)(i + 1) * V, V), c, x1);
-        publish_part<M>(a, row0 + i, c, block_reduce<M, false>(thread_stats<M, kVecG>(x0, x0, c), 0));
-        if (i + 1 >= r1) break;
-        if (i + 2 < r1) load_chunk<VEC, kVecG>(row_of(tb + (int64_t)(i + 2) * V, V), c, x0);
-        publish_part<M>(a, row0 + i + 1, c, block_reduce<M, false>(thread_stats<M, kVecG>(x1, x1, c), 1));
-    }
-    if (c != finisher_column(b, NC) || seg != S - 1) return;
+    const int64_t row = (int64_t)b * (K + 1) + r;
+    float4 x[kVecG];
+    load_chunk<VEC, kVecG>(row_of(a.tp + row * V, V), c, x);
+    publish_part<M>(a, row, c, block_reduce<M, false>(thread_stats<M, kVecG>(x, x, c), 0));
+    if (c != finisher_column(b, NC) || r != K) return;
 
     const Outcome o = finish_rows<VEC, false, kVecG, M, M>(lds_greedy, a, b);
     if (threadIdx.x == 0) {
@@ -2317,6 +2308,33 @@ bool use_rows(int K, uint64_t per_row, uint64_t bonus, uint64_t per_draft_row, c
     return (uint64_t)K * per_row + bonus <= per_draft_row * (uint64_t)(K > 4 ? K : 4);
 }
 
+// The greedy kernel needs little LDS, so up to 8 of its blocks would share a
+// CU; measured, 4 (the residency of the sampled pass) streams faster: 8192-
+// value chunks at B=256 K=5 V=128256 take 115 instead of 118 µs, at B=32 K=16
+// V=262144 83.4 instead of 85.1 µs (3 per CU: 123 and 89 µs).  A launch of
+// more blocks than fit at once uncapped (8 per CU) therefore asks for dynamic
+// LDS up to kGreedyLdsPerBlock per block: 4 x 36 KB fit in a CU's 160 KB, 5
+// do not.  A smaller grid (B=64 K=4 V=32000: 1280 blocks) stays uncapped, all
+// of it resident at once.  The kernel's own static LDS is read once.
+template <bool VEC, bool STATS>
+unsigned greedy_lds_pad()
+{
+    static const unsigned pad = [] {
+        hipFuncAttributes fa{};
+        if (hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(&sv_greedy_kernel<VEC, STATS>)) != hipSuccess)
+            return 0u;
+        return fa.sharedSizeBytes < kGreedyLdsPerBlock ? (unsigned)(kGreedyLdsPerBlock - fa.sharedSizeBytes) : 0u;
+    }();
+    return pad;
+}
+
+template <bool VEC, bool STATS>
+void launch_greedy(dim3 grid, hipStream_t s, const Args& a)
+{
+    const unsigned pad = grid.x > kGreedyUncappedBlocks ? greedy_lds_pad<VEC, STATS>() : 0u;
+    hipLaunchKernelGGL((sv_greedy_kernel<VEC, STATS>), grid, dim3(kThreads), pad, s, a);
+}
+
 template <bool VEC, bool STATS>
 void launch_sample(bool rows, dim3 grid, hipStream_t s, const Args& a)
 {
@@ -2446,17 +2464,15 @@ sv_status sv_verify_greedy_batched(const float* target_probs, const int32_t* dra
     a.force_recompute = tu.force_recompute;
     a.poll_ticks = (unsigned long long)(tu.poll_us * 1e-3 * (double)d.wall_khz);
     const bool vec = (V % 4 == 0) && aligned(target_probs, 16);
-    a.walk_rows = kGreedyWalkRows < K + 1 ? kGreedyWalkRows : K + 1;
-    const uint64_t segs = (uint64_t)(K + a.walk_rows) / (uint64_t)a.walk_rows;
-    const dim3 grid((unsigned)((uint64_t)B * segs * (uint64_t)a.NC)), block(kThreads);
+    const dim3 grid((unsigned)((uint64_t)B * (uint64_t)(K + 1) * (uint64_t)a.NC));
     if (vec && stats)
-        hipLaunchKernelGGL((sv_greedy_kernel<true, true>), grid, block, 0, s, a);
+        launch_greedy<true, true>(grid, s, a);
     else if (vec)
-        hipLaunchKernelGGL((sv_greedy_kernel<true, false>), grid, block, 0, s, a);
+        launch_greedy<true, false>(grid, s, a);
     else if (stats)
-        hipLaunchKernelGGL((sv_greedy_kernel<false, true>), grid, block, 0, s, a);
+        launch_greedy<false, true>(grid, s, a);
     else
-        hipLaunchKernelGGL((sv_greedy_kernel<false, false>), grid, block, 0, s, a);
+        launch_greedy<false, false>(grid, s, a);
     return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
