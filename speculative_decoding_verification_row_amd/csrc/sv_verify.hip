@@ -2321,8 +2321,10 @@ unsigned greedy_lds_pad()
 {
     static const unsigned pad = [] {
         hipFuncAttributes fa{};
-        if (hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(&sv_greedy_kernel<VEC, STATS>)) != hipSuccess)
+        if (hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(&sv_greedy_kernel<VEC, STATS>)) != hipSuccess) {
+            (void)hipGetLastError();   // no pad then; the launch must not report this query's error
             return 0u;
+        }
         return fa.sharedSizeBytes < kGreedyLdsPerBlock ? (unsigned)(kGreedyLdsPerBlock - fa.sharedSizeBytes) : 0u;
     }();
     return pad;
