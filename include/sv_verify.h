@@ -90,9 +90,13 @@ size_t sv_workspace_size(int32_t B, int32_t K, int32_t V, int32_t sampled);
 
 /* Zero a workspace on `stream` (a fill kernel; no memset node) and restart
  * its call count.  Memory must be initialised this way before its first use
- * as a workspace (the first call on an address the library has not seen also
- * clears it).  Afterwards calls need no further initialisation: every 255th
- * call on a workspace clears it again on its stream before it runs.
+ * as a workspace, and again whenever it has held other data since it was
+ * last used as one (for example a buffer freed and allocated anew at the
+ * same address).  The first call on an address the library has not seen,
+ * and a call with more workspace bytes than any earlier call at that
+ * address, also clear it first.  Otherwise calls need no further
+ * initialisation: every 255th call on a workspace clears it again on its
+ * stream before it runs.
  * Errors: SV_ERR_WORKSPACE for NULL or non-16-byte-aligned memory,
  * SV_ERR_HIP when the launch fails. */
 sv_status sv_workspace_init(void* workspace, size_t workspace_bytes, void* stream);

@@ -38,11 +38,14 @@
 //
 // Cross-block data and progress.  There are no counters and no
 // read-modify-write atomics in global memory.  Every published 8-byte word
-// carries the call's epoch (1..255, chosen by the host per workspace) in
-// bits that readers strip: the low 8 mantissa bits of an fp64 partial (a
-// relative change below 2^-44, the same for every reader) or the top byte of
-// an (argmax, max) word.  A reader polls until each word it needs carries
-// the current epoch.  If a word has not arrived within a time bound (its
+// carries the call's epoch (1..255, chosen by the host per workspace) in its
+// low byte, which readers strip: the low 8 mantissa bits of an fp64 partial
+// (a relative change below 2^-44, the same for every reader), the byte below
+// the argmax of a (max, argmax) word, the byte below the outcome code of a
+// sequence's outcome word.  The position is the same for every kind of word,
+// so a word an earlier call left at an address this call reads, whatever
+// its kind, shows that call's epoch.  A reader polls until each word it
+// needs carries the current epoch.  If a word has not arrived within a time bound (its
 // producer has not been scheduled), the reader computes that partial itself
 // with the producer's arithmetic in the producer's order, so the value is
 // bit-identical.  No wait is unbounded, and correctness never depends on the
@@ -89,7 +92,7 @@ struct Header {              // 256 bytes
 
 struct Part {                // 32 bytes, one per (row, chunk); tagged words
     unsigned long long sp, sq, smin;   // fp64 chunk sums of p, q, min(p, q)
-    unsigned long long am;             // max value (low 32 bits), argmax (bits 32..55)
+    unsigned long long am;             // max value (high 32 bits), argmax (bits 8..31)
 };
 
 struct Layout {
@@ -165,13 +168,21 @@ __device__ __forceinline__ double f64_of(unsigned long long w)
 // the value every reader obtains for a published fp64 partial
 __device__ __forceinline__ double strip8(double v) { return f64_of((unsigned long long)__double_as_longlong(v)); }
 
+// A (value, argmax) word: the value's bits in the high 32 bits, the argmax
+// (24 bits; positions are below 2^19) in bits 8..31, and the tag in the low
+// byte like every other published word.  One tag position for every kind of
+// word matters: workspace addresses serve different layouts from call to
+// call, so a reader may find, where it expects its word, a word another
+// call left there of another kind; that word's low byte is then that call's
+// tag, never this call's.
 __device__ __forceinline__ unsigned long long tag_am(float v, int arg, unsigned ep)
 {
-    return ((unsigned long long)((ep << 24) | (unsigned)arg) << 32) | (unsigned long long)__float_as_uint(v);
+    return ((unsigned long long)__float_as_uint(v) << 32) | ((unsigned long long)((unsigned)arg & 0xFFFFFFu) << 8) |
+           ep;
 }
-__device__ __forceinline__ bool am_ok(unsigned long long w, unsigned ep) { return (unsigned)(w >> 56) == ep; }
-__device__ __forceinline__ float am_val(unsigned long long w) { return __uint_as_float((unsigned)w); }
-__device__ __forceinline__ int am_arg(unsigned long long w) { return (int)((w >> 32) & 0xFFFFFFu); }
+__device__ __forceinline__ bool am_ok(unsigned long long w, unsigned ep) { return (w & 0xFFull) == ep; }
+__device__ __forceinline__ float am_val(unsigned long long w) { return __uint_as_float((unsigned)(w >> 32)); }
+__device__ __forceinline__ int am_arg(unsigned long long w) { return (int)((w >> 8) & 0xFFFFFFu); }
 
 // Block-uniform bounded wait: true once the bound has passed (thread 0's
 // clock decides, so every thread leaves the wait loop together).
@@ -1197,7 +1208,8 @@ __device__ __forceinline__ void finish_bonus(const Args& a, int b)
             if (threadIdx.x == 0) {
                 const unsigned long long v = get_u64(&a.sstate[b]);
                 got = f64_ok(v, a.epoch) && !a.force_recompute;
-                s_code = got ? (int)(v >> 8) : 0;
+                const unsigned long long code = v >> 8;
+                s_code = got && code <= (unsigned long long)(K + 1) ? (int)code : 0;   // 0: decide here
             }
             if (__syncthreads_or(got)) break;
             if (wait_expired(a, t0)) break;
@@ -2063,7 +2075,8 @@ __device__ int wait_state_l(const Args& a, int b)
         if (threadIdx.x == 0) {
             const unsigned long long v = get_u64(&a.sstate[b]);
             got = f64_ok(v, a.epoch) && !a.force_recompute;
-            s_code = got ? (int)(v >> 8) : 0;
+            const unsigned long long code = v >> 8;
+            s_code = got && code <= (unsigned long long)(a.K + 1) ? (int)code : 0;   // 0: decide here
         }
         if (__syncthreads_or(got)) break;
         if (wait_expired(a, t0)) break;
@@ -2366,10 +2379,11 @@ sv_status launch_fill(void* ws, size_t bytes, hipStream_t s)
 }
 
 // The tag of this call on `ws` (1..kEpochs).  Each tag is used once between
-// clears: the first call on a workspace the library has not seen, and every
-// call after kEpochs tags have been used, clears the whole extent of the
-// workspace seen so far on `s` first, so no word left by an earlier call can
-// carry a tag in use.
+// clears: the first call on a workspace the library has not seen, a call
+// with more bytes than any earlier call at that address (the new part was
+// never cleared), and every call after kEpochs tags have been used clear the
+// whole extent of the workspace seen so far on `s` first, so no word left by
+// an earlier call can carry a tag in use.
 sv_status next_epoch(void* ws, size_t bytes, hipStream_t s, unsigned* ep)
 {
     bool clear = false;
@@ -2382,7 +2396,10 @@ sv_status next_epoch(void* ws, size_t bytes, hipStream_t s, unsigned* ep)
             it->second.calls = kEpochs;   // unknown contents: clear first
         }
         WsState& st = it->second;
-        if (bytes > st.bytes) st.bytes = bytes;
+        if (bytes > st.bytes) {   // the part beyond the extent cleared so far holds unknown words
+            st.bytes = bytes;
+            st.calls = kEpochs;
+        }
         if (st.calls >= kEpochs) {
             st.calls = 0;
             clear = true;

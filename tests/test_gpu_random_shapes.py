@@ -1,0 +1,118 @@
+"""GPU parity on seeded random shapes: B, K and V drawn at random (V
+log-uniform up to 70000, so one to eighteen 4096-value chunks with ragged
+tails; K = 0 for every eighth), greedy, sampled and logits, statistics on and
+off, the sampled and logits form (walks or one block per row) left to the
+library or forced, in turn.  Every
+sequence is compared with the fp64 oracle to the bars of the other parity
+tests: greedy bit for bit, sampled and logits identical outside the 1e-5
+boundary band."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle.logits import verify_sample_logits
+import speculative_decoding_verification_row_amd as sv
+
+from _parity import check_greedy, check_sampled
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+N_SHAPES = 24
+
+
+def _case(msg):
+    print(f"\n[gpu case] {msg}", flush=True)
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    sv.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def _shape(j):
+    """B up to 64, K up to 12, V log-uniform over [2, 70000] (half the shapes
+    over [10000, 70000]), the whole batch kept under 3e7 values so that the
+    oracle finishes in a second or two."""
+    rng = np.random.default_rng(9000 + j)
+    B = int(rng.integers(1, 65))
+    K = 0 if j % 8 == 7 else int(rng.integers(1, 13))
+    lo = np.log(10000.0) if j % 4 < 2 else np.log(2.0)
+    V = int(np.exp(rng.uniform(lo, np.log(70000.0))))
+    while B > 1 and B * (2 * K + 1) * V > 3e7:
+        B //= 2
+    return B, K, V, rng
+
+
+# every third shape leaves the sampled form to the library's size rule (which
+# picks one block per row at these sizes); the others force walks or rows
+FORMS = ("auto", "walks", "rows")
+
+
+def _rows(rng, B, K, V):
+    """Unnormalised rows with zeros and tied maxima; draft tokens from q
+    half the time, else the target's argmax or a random token."""
+    p = rng.random((B, K + 1, V)).astype(np.float32) * rng.uniform(0.5, 2.0, (B, K + 1, 1)).astype(np.float32)
+    q = rng.random((B, K, V)).astype(np.float32)
+    p[rng.random(p.shape) < 0.15] = 0
+    p[..., 0] += np.float32(1e-3)
+    q[..., -1] += np.float32(1e-3)
+    for b in range(B):
+        for i in range(K + 1):
+            p[b, i, rng.choice(V, size=min(V, 2), replace=False)] = p[b, i].max()
+    t = np.empty((B, K), np.int32)
+    for b in range(B):
+        for i in range(K):
+            r = rng.random()
+            if r < 0.5:
+                c = np.cumsum(q[b, i].astype(np.float64))
+                t[b, i] = min(int(np.searchsorted(c, rng.random() * c[-1], side="right")), V - 1)
+            elif r < 0.8:
+                t[b, i] = int(np.argmax(p[b, i]))
+            else:
+                t[b, i] = int(rng.integers(0, V))
+    u = rng.random((B, K + 1), dtype=np.float32)
+    return p, q, t, u
+
+
+def _dev(*arrays):
+    return [torch.from_numpy(np.ascontiguousarray(a)).to(DEV) for a in arrays]
+
+
+@pytest.mark.parametrize("j", range(N_SHAPES))
+def test_random_shape(j, monkeypatch):
+    B, K, V, rng = _shape(j)
+    stats = bool(j % 2)
+    form = FORMS[j % 3]
+    if form != "auto":
+        monkeypatch.setenv("SV_VERIFY_ROWS", "1" if form == "rows" else "0")
+    _case(f"random shape {j}: B={B} K={K} V={V} stats={stats} sampled form={form}")
+    p, q, t, u = _rows(rng, B, K, V)
+    tp, dp, dt, ud = _dev(p, q, t, u)
+
+    r = sv.sv_verify_greedy_batched(tp, dt, stats=stats or None)
+    torch.cuda.synchronize()
+    check_greedy(r[0].cpu().numpy(), r[1].cpu().numpy(),
+                 sv.stats_to_numpy(r[2]) if stats else None, oracle.verify_greedy(p, t))
+
+    r = sv.sv_verify_sample_batched(tp, dp, dt, ud, stats=stats or None)
+    torch.cuda.synchronize()
+    check_sampled(r[0].cpu().numpy(), r[1].cpu().numpy(),
+                  sv.stats_to_numpy(r[2]) if stats else None, oracle.verify_sample(p, q, t, u))
+
+    # the same rows read as logits (their log, with -1e4 for zeros), one temperature
+    tau = float(rng.choice([0.7, 1.0, 1.6]))
+    lp = np.where(p > 0, np.log(np.maximum(p, 1e-30)), -1e4).astype(np.float32)
+    lq = np.where(q > 0, np.log(np.maximum(q, 1e-30)), -1e4).astype(np.float32)
+    tl, dl = _dev(lp, lq)
+    n, nx = sv.sv_verify_sample_logits_batched(tl, dl, dt, ud, tau)
+    torch.cuda.synchronize()
+    o = verify_sample_logits(lp, lq, t, u, tau)
+    d = o["diag"]
+    bnd = (d["accept_margin"] <= 1e-5) | (d["draw_margin"] <= 1e-5) | (d["draw_kind"] >= 4)
+    same = (n.cpu().numpy() == o["n_accepted"]) & (nx.cpu().numpy() == o["next_token"])
+    assert not (~same & ~bnd).any(), f"logits: {int((~same & ~bnd).sum())} non-boundary mismatches"
