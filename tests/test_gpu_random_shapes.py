@@ -116,3 +116,64 @@ def test_random_shape(j, monkeypatch):
     bnd = (d["accept_margin"] <= 1e-5) | (d["draw_margin"] <= 1e-5) | (d["draw_kind"] >= 4)
     same = (n.cpu().numpy() == o["n_accepted"]) & (nx.cpu().numpy() == o["next_token"])
     assert not (~same & ~bnd).any(), f"logits: {int((~same & ~bnd).sum())} non-boundary mismatches"
+
+
+def _shape_wide(j):
+    """Shapes the first set does not reach: large batches over small V (the
+    library's own rule then picks walks), long drafts (K up to 32), and
+    every third shape's rows at a 4- but not 16-byte aligned address."""
+    rng = np.random.default_rng(19000 + j)
+    if j % 2 == 0:
+        B = int(rng.integers(300, 900))
+        K = int(rng.integers(1, 5))
+        V = int(rng.integers(2, 4097))
+    else:
+        B = int(rng.integers(1, 9))
+        K = int(rng.integers(8, 33))
+        V = int(np.exp(rng.uniform(np.log(2.0), np.log(40000.0))))
+    while B > 1 and B * (2 * K + 1) * V > 3e7:
+        B //= 2
+    return B, K, V, j % 3 == 2, rng
+
+
+def _dev_offset(a):
+    """A copy of `a` on the device, one float past a 16-byte boundary."""
+    flat = np.ascontiguousarray(a).reshape(-1)
+    buf = torch.zeros(flat.size + 1, dtype=torch.float32, device=DEV)
+    buf[1:].copy_(torch.from_numpy(flat))
+    return buf[1:].view(a.shape)
+
+
+@pytest.mark.parametrize("j", range(N_SHAPES))
+def test_random_shape_wide(j):
+    B, K, V, unaligned, rng = _shape_wide(j)
+    stats = bool(j % 4 == 1)
+    _case(f"random wide shape {j}: B={B} K={K} V={V} unaligned={unaligned} stats={stats}")
+    p, q, t, u = _rows(rng, B, K, V)
+    dt, ud = _dev(t, u)
+    if unaligned:
+        tp, dp = _dev_offset(p), _dev_offset(q)
+    else:
+        tp, dp = _dev(p, q)
+
+    r = sv.sv_verify_greedy_batched(tp, dt, stats=stats or None)
+    torch.cuda.synchronize()
+    check_greedy(r[0].cpu().numpy(), r[1].cpu().numpy(),
+                 sv.stats_to_numpy(r[2]) if stats else None, oracle.verify_greedy(p, t))
+
+    r = sv.sv_verify_sample_batched(tp, dp, dt, ud, stats=stats or None)
+    torch.cuda.synchronize()
+    check_sampled(r[0].cpu().numpy(), r[1].cpu().numpy(),
+                  sv.stats_to_numpy(r[2]) if stats else None, oracle.verify_sample(p, q, t, u))
+
+    tau = float(rng.choice([0.8, 1.0, 1.3]))
+    lp = np.where(p > 0, np.log(np.maximum(p, 1e-30)), -1e4).astype(np.float32)
+    lq = np.where(q > 0, np.log(np.maximum(q, 1e-30)), -1e4).astype(np.float32)
+    tl, dl = (_dev_offset(lp), _dev_offset(lq)) if unaligned else _dev(lp, lq)
+    n, nx = sv.sv_verify_sample_logits_batched(tl, dl, dt, ud, tau)
+    torch.cuda.synchronize()
+    o = verify_sample_logits(lp, lq, t, u, tau)
+    d = o["diag"]
+    bnd = (d["accept_margin"] <= 1e-5) | (d["draw_margin"] <= 1e-5) | (d["draw_kind"] >= 4)
+    same = (n.cpu().numpy() == o["n_accepted"]) & (nx.cpu().numpy() == o["next_token"])
+    assert not (~same & ~bnd).any(), f"logits: {int((~same & ~bnd).sum())} non-boundary mismatches"
