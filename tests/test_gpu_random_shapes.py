@@ -177,3 +177,47 @@ def test_random_shape_wide(j):
     bnd = (d["accept_margin"] <= 1e-5) | (d["draw_margin"] <= 1e-5) | (d["draw_kind"] >= 4)
     same = (n.cpu().numpy() == o["n_accepted"]) & (nx.cpu().numpy() == o["next_token"])
     assert not (~same & ~bnd).any(), f"logits: {int((~same & ~bnd).sum())} non-boundary mismatches"
+
+
+def test_layout_churn_across_tag_wrap():
+    """300 calls on one workspace, cycling through five shapes and the three
+    entry points, so that every call reads over words that calls of other
+    layouts and kinds left behind, and the tags wrap around once: every
+    output stays the oracle's (each shape's inputs are the same every time
+    it comes round)."""
+    _case("layout churn: 300 calls on one workspace across the tag wrap")
+    shapes = [(3, 4, 5000), (40, 2, 326), (7, 9, 9000), (1, 1, 70001), (64, 3, 1500)]
+    cases = []
+    need = 0
+    for s, (B, K, V) in enumerate(shapes):
+        rng = np.random.default_rng(31000 + s)
+        p, q, t, u = _rows(rng, B, K, V)
+        lp = np.where(p > 0, np.log(np.maximum(p, 1e-30)), -1e4).astype(np.float32)
+        lq = np.where(q > 0, np.log(np.maximum(q, 1e-30)), -1e4).astype(np.float32)
+        og, os_, ol = oracle.verify_greedy(p, t), oracle.verify_sample(p, q, t, u), verify_sample_logits(lp, lq, t, u, 1.0)
+        cases.append(((B, K, V), _dev(p, q, t, u, lp, lq), og, os_, ol))
+        need = max(need, sv.sv_workspace_size(B, K, V, True))
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    sv.sv_workspace_init(ws)
+    for j in range(300):
+        (B, K, V), (tp, dp, dt, ud, tl, dl), og, os_, ol = cases[j % len(cases)]
+        kind = (j // len(cases)) % 3
+        if kind == 0:
+            n, nx = sv.sv_verify_greedy_batched(tp, dt, workspace=ws)
+            ref = og
+        elif kind == 1:
+            n, nx = sv.sv_verify_sample_batched(tp, dp, dt, ud, workspace=ws)
+            ref = os_
+        else:
+            n, nx = sv.sv_verify_sample_logits_batched(tl, dl, dt, ud, 1.0, workspace=ws)
+            ref = ol
+        torch.cuda.synchronize()
+        n, nx = n.cpu().numpy(), nx.cpu().numpy()
+        if kind == 0:
+            assert np.array_equal(n, ref["n_accepted"]) and np.array_equal(nx, ref["next_token"]), (j, B, K, V)
+        else:
+            d = ref["diag"]
+            bnd = (d["accept_margin"] <= 1e-5) | (d["draw_margin"] <= 1e-5) | (d["draw_kind"] >= 4)
+            same = (n == ref["n_accepted"]) & (nx == ref["next_token"])
+            assert not (~same & ~bnd).any(), (j, kind, B, K, V)
+    assert sv.sv_workspace_error(ws) == 0
