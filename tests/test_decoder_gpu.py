@@ -112,3 +112,35 @@ def test_gpu_device_resident_callbacks():
         if greedy:
             assert out == greedy_decode(target, [4, 2], 25)
         assert len(out) == 27
+
+
+@pytest.mark.parametrize("j", range(12))
+def test_gpu_random_decoder_configs(j):
+    """Seeded random driver settings (V, k from 0 to 5, greedy or sampled,
+    batched or not, with or without a governor, several prompts of random
+    lengths): greedy streams equal plain greedy decoding of the target, and
+    every stream equals the one the oracle-driven driver emits for the same
+    seeds."""
+    rng = np.random.default_rng(500 + j)
+    V = int(rng.choice([7, 300, 5000, 40000]))
+    k = int(rng.integers(0, 6))
+    greedy = bool(j % 2)
+    batched = bool((j // 2) % 2)
+    gov = Governor(alpha_threshold=float(rng.uniform(0.0, 0.6)), window=int(rng.integers(1, 5))) if j % 3 == 0 else None
+    nprompt = int(rng.integers(1, 6)) if batched else 1
+    prompts = [[int(x) for x in rng.integers(0, V, size=int(rng.integers(1, 5)))] for _ in range(nprompt)]
+    max_new = int(rng.integers(1, 30))
+    _case(f"random decoder config {j}: V={V} k={k} greedy={greedy} batched={batched} "
+          f"governor={gov is not None} prompts={nprompt} max_new={max_new}")
+    target = HashLM(V, sigma=2.0, salt=600 + j)
+    draft = HashLM(V, salt=700 + j, base=target, noise=float(rng.uniform(0.3, 2.0)))
+    outs = []
+    for verify in (None, oracle_verify(greedy)):
+        ds, ts = make_callbacks(target, draft, greedy=greedy, seed=j, batched=batched)
+        dec = SpeculativeDecoder(ds, ts, k=k, greedy=greedy, seed=j + 1, batched=batched, verify=verify,
+                                 governor=gov)
+        outs.append(dec.generate(prompts if batched else prompts[0], max_new=max_new))
+    assert outs[0] == outs[1]
+    if greedy:
+        want = [greedy_decode(target, p, max_new) for p in prompts]
+        assert (outs[0] if batched else [outs[0]]) == want
