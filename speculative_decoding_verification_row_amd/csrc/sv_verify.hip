@@ -133,6 +133,7 @@ struct Args {
     int force_recompute;             // test hook: readers recompute every partial
     unsigned long long poll_ticks;   // wait bound in wall-clock ticks
     float ktau;                      // logits: log2(e) / temperature
+    double ktau64;                   // the same in fp64 (acceptance weights)
 };
 
 // ------------------------------------------- cross-block communication --
@@ -527,7 +528,7 @@ __device__ __forceinline__ double sum_chunks(const double* s, int NC)
 
 // The acceptance test of a draft token (fp64, scale-free): accept iff
 // u * q(t) * P < p(t) * Q.  Every place that decides uses this expression.
-__device__ __forceinline__ bool accepted(float u, float pt, float qt, double P, double Q)
+__device__ __forceinline__ bool accepted(float u, double pt, double qt, double P, double Q)
 {
     return (double)u * (double)qt * P < (double)pt * Q;
 }
@@ -1410,15 +1411,41 @@ __global__ __launch_bounds__(kThreads, 4) void sv_sample_kernel(Args a)
 // thread in fp32, then across the wave in fp64), and the chunk rescales the
 // four wave sums to m_c in wave order.  A reader of a row takes its maximum M
 // (the largest m_c) and its mass sum_c s_c exp2((m_c - M) * k), in chunk
-// order.  Single weights (p(t), q(t), the residual, the draws) are
-// exp2((l - M) * k) against the same M, on the scale of that mass.
+// order (chunk_scaled).  Single weights (the residual, the draws) are
+// exp2((l - M) * k) against the same M, on the scale of that mass; the two
+// weights of an acceptance test take more care over range and rounding
+// (accepted_l).
 
-// The argument is one fused multiply-add, l * k - m * k: the rounding of
-// m * k is shared by the whole row, so it scales every weight of the row
-// alike and cancels in the normalised distribution.
+// The weight of a logit l against a maximum m: exp2(l * k - r) with
+// r = m * k rounded to fp32, the argument one fused multiply-add (l * k
+// exact inside it).  Every weight taken against the same m shares the one
+// rounding of r; weights taken against different maxima are brought to a
+// common one by chunk_scaled, which uses the same rounded products, so the
+// rounding cancels there too.
 __device__ __forceinline__ float lweight(float l, float m, float k)
 {
     return __builtin_amdgcn_exp2f(__builtin_fmaf(l, k, -(m * k)));
+}
+
+// The weight of a draft token's logit for its acceptance test, with fp64
+// range and an fp64 temperature.  At a low temperature a token far from its
+// row's maximum has an exponent far below fp32's range (-650 for a logit 9
+// below the maximum at tau 0.02): in fp32 both of its weights would flush to
+// zero and decide 0 < 0, whatever the ratio p(t)/q(t) they stand for; and
+// the fp32 k = log2(e) / tau, exact to 6e-8 relative, would move an exponent
+// of -650 by 4e-5.  The exponent here is (l - m) * k64 plus the rounding
+// m * k - r of the row's shared scale r = m * k (fp32): the row mass carries
+// the factor 2^(m k - r) in every weight, so it still cancels in the test.
+// It splits exactly into n = floor(e) and f = e - n in [0, 1), and the weight
+// is 2^f (fp32, f rounded by at most 2^-25) scaled by 2^n in fp64: about
+// 1.5e-7 relative in all.  -inf logits give 0.
+__device__ __forceinline__ double lweight_wide(float l, float m, float k, double k64)
+{
+    const float r = m * k;
+    const double e = __builtin_fma((double)l - (double)m, k64, __builtin_fma((double)m, (double)k, -(double)r));
+    if (!(e > -1100.0)) return e != e ? e : 0.0;   // NaN stays NaN (rejects); below fp64's range, 0
+    const double n = __builtin_floor(e);
+    return __builtin_ldexp((double)__builtin_amdgcn_exp2f((float)(e - n)), (int)n);
 }
 
 // Maximum over the wave (all 64 lanes active), the same in every lane.
@@ -1489,10 +1516,20 @@ __device__ __forceinline__ double share_wsum(const float4 (&v)[NV], float m, flo
     return (double)s;
 }
 
-// A chunk sum s against maximum m, rescaled to reference M (0 for an empty chunk).
+// A chunk sum s of weights taken against maximum m, rescaled to reference M
+// (0 for an empty chunk): s * exp2(r_m - r_M), r_x = x * k rounded to fp32 as
+// in lweight.  The rounding of r_m in the chunk's weights cancels, and that
+// of r_M is the one every weight against M carries.  The difference of the
+// two products is exact when they lie within a factor of 2 of each other and
+// otherwise rounded once, like any weight's own argument.  The exact m * k
+// of an fma here instead would leave the rounding of r_m in every weight of
+// the chunk: at tau = 0.02 (k = 72, |m * k| ~ 600) that is 2e-5 of the row's
+// mass.
 __device__ __forceinline__ double chunk_scaled(float m, double s, float M, float k)
 {
-    return m == -INFINITY ? 0.0 : s * (double)lweight(m, M, k);
+    if (m == -INFINITY) return 0.0;
+    const float rm = m * k, rM = M * k;   // not contracted: fp contract is off in this file
+    return s * (double)__builtin_amdgcn_exp2f(rm - rM);
 }
 
 struct LStat {
@@ -1585,6 +1622,34 @@ struct LRow {
     double P, Q;
     float Mp, Mq;
 };
+
+// The acceptance test of a draft token on logits, for exponents outside
+// [-16, 0]: the token weights with fp64 range and temperature (lweight_wide).
+// Not inlined, so that its fp64 work adds nothing to the registers of the
+// streaming loops it is reached from.  Everything it needs comes in as
+// arguments: inside a called function the kernel-argument segment pointer
+// is not available (the compiler materialises it as null).
+__device__ __noinline__ bool accepted_wide_l(float u, float lp, float lq, float Mp, float Mq, double P, double Q,
+                                             float k, double k64)
+{
+    return accepted(u, lweight_wide(lp, Mp, k, k64), lweight_wide(lq, Mq, k, k64), P, Q);
+}
+
+// The acceptance test of draft token logits lp = l_p(t), lq = l_q(t) against
+// row r (tin: the token is inside [0, V); a token outside is rejected).
+// Where both fp32 exponents lie in [-16, 0] the fp32 weights serve: the
+// rounding of k (6e-8 relative) and of the exponents moves the ratio
+// p(t)/q(t) by under 3e-6 there.  Elsewhere the fp64 test decides.  Every
+// place that decides a logits row uses this function.
+__device__ __forceinline__ bool accepted_l(bool tin, float u, float lp, float lq, const LRow& r, float k, double k64)
+{
+    if (!tin) return false;
+    const float ap = __builtin_fmaf(lp, k, -(r.Mp * k));
+    const float aq = __builtin_fmaf(lq, k, -(r.Mq * k));
+    if (ap >= -16.0f && aq >= -16.0f)
+        return accepted(u, __builtin_amdgcn_exp2f(ap), __builtin_amdgcn_exp2f(aq), r.P, r.Q);
+    return accepted_wide_l(u, lp, lq, r.Mp, r.Mq, r.P, r.Q, k, k64);
+}
 
 // The walk's poll of row i: lane c < min(NC, 64) of wave 0 reads chunk c's
 // four words; lane 0 also the logits at the draft token and the uniform.
@@ -1682,10 +1747,8 @@ __device__ int poll_decide_l(const Args& a, int b, int i, PollL pl, LRow* out)
             r.P = row_mass_l(m0p, s0p, m1p, s1p, k, &r.Mp);
             r.Q = row_mass_l(m0q, s0q, m1q, s1q, k, &r.Mq);
             if (t == 0) {
-                const float ept = pl.tin ? lweight(pl.pt, r.Mp, k) : 0.0f;
-                const float eqt = pl.tin ? lweight(pl.qt, r.Mq, k) : 0.0f;
                 s_row = r;
-                s_rej = accepted(pl.u, ept, eqt, r.P, r.Q) ? 0 : 1;
+                s_rej = accepted_l(pl.tin, pl.u, pl.pt, pl.qt, r, k, a.ktau64) ? 0 : 1;
             }
         } else if (t == 0) {
             s_rej = -1;
@@ -2047,9 +2110,8 @@ __device__ __noinline__ LDecision decide_rows_l(const Args& a, int b)
         if (threadIdx.x == 0) {
             const int tk = a.dt[(int64_t)b * K + i];
             const bool tin = tk >= 0 && tk < V;
-            const float ept = tin ? lweight(a.tp[(row0 + i) * V + tk], r.Mp, a.ktau) : 0.0f;
-            const float eqt = tin ? lweight(a.dp[((int64_t)b * K + i) * V + tk], r.Mq, a.ktau) : 0.0f;
-            s_rej = accepted(a.u[row0 + i], ept, eqt, r.P, r.Q) ? 0 : 1;
+            s_rej = accepted_l(tin, a.u[row0 + i], tin ? a.tp[(row0 + i) * V + tk] : 0.0f,
+                               tin ? a.dp[((int64_t)b * K + i) * V + tk] : 0.0f, r, a.ktau, a.ktau64) ? 0 : 1;
         }
         __syncthreads();
         const int rej = s_rej;
@@ -2580,7 +2642,8 @@ sv_status sv_verify_sample_logits_batched(const float* target_logits, const floa
     a.n_out = n_accepted;
     a.next_out = next_token;
     // exp(x / tau) = exp2(x * log2(e) / tau)
-    a.ktau = (float)(1.4426950408889634 / (double)temperature);
+    a.ktau64 = 1.4426950408889634 / (double)temperature;
+    a.ktau = (float)a.ktau64;
     const Tuning tu = tuning();
     a.force_recompute = tu.force_recompute;
     a.poll_ticks = (unsigned long long)(tu.poll_us * 1e-3 * (double)d.wall_khz);

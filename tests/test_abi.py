@@ -125,3 +125,29 @@ def test_binding_without_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(sv, "_LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         sv.load_library()
+
+
+def _enclosing_function(text, pos):
+    """The header line of the top-level function whose body holds `pos`:
+    the last line before it that starts a definition at column 0."""
+    heads = [m for m in re.finditer(r"^(?:__global__|__device__|static|template|sv_status|extern)[^\n]*$",
+                                     text[:pos], flags=re.M)]
+    return heads[-1].group(0) if heads else ""
+
+
+def test_kernel_argument_pointer_is_taken_in_kernel_bodies_only():
+    """Inside a called (non-kernel) device function the kernel-argument
+    segment pointer is not available: the compiler materialises it as null,
+    and a read through it faults.  Every use of the builtin must therefore
+    sit in a __global__ function's body, which passes the pointer or the
+    values down."""
+    src = os.path.join(ROOT, "speculative_decoding_verification_row_amd", "csrc", "sv_verify.hip")
+    text = open(src).read()
+    uses = [m.start() for m in re.finditer(r"__builtin_amdgcn_kernarg_segment_ptr\s*\(", text)]
+    assert uses
+    for pos in uses:
+        line = text.count("\n", 0, pos) + 1
+        if text.rfind("//", text.rfind("\n", 0, pos), pos) >= 0:
+            continue                                            # a comment
+        head = _enclosing_function(text, pos)
+        assert head.startswith("__global__"), f"line {line}: inside `{head}`"

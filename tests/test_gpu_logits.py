@@ -206,3 +206,15 @@ def test_logits_argument_errors():
             sv.sv_verify_sample_logits_batched(tl, dl, t, u, bad)
     n, nx = sv.sv_verify_sample_logits_batched(tl, dl, t, u, 1.0)
     assert int(n.item()) == 1 and int(nx.item()) == 0
+
+
+@pytest.mark.parametrize("tau", [0.02, 50.0])
+@pytest.mark.parametrize("B,K,V", [(4, 3, 5000), (2, 5, 40001)], ids=lambda x: str(x))
+def test_logits_extreme_temperatures(B, K, V, tau, form):
+    """A very low temperature (most fp32 weights underflow to 0, where the
+    fp64 oracle keeps them, far below the 1e-5 band) and a very high one
+    (nearly flat rows)."""
+    _case(f"logits extreme tau={tau} B={B} K={K} V={V} form={form}")
+    rng = np.random.default_rng(int(tau * 100) + B + K + V)
+    lp, lq, t, u = _rows(rng, B, K, V, tau)
+    check(*run(lp, lq, t, u, tau), verify_sample_logits(lp, lq, t, u, tau))
