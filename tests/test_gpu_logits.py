@@ -218,3 +218,23 @@ def test_logits_extreme_temperatures(B, K, V, tau, form):
     rng = np.random.default_rng(int(tau * 100) + B + K + V)
     lp, lq, t, u = _rows(rng, B, K, V, tau)
     check(*run(lp, lq, t, u, tau), verify_sample_logits(lp, lq, t, u, tau))
+
+
+@pytest.mark.parametrize("B,K,V", [(300, 4, 700), (8, 5, 40001), (256, 5, 128256)], ids=lambda x: str(x))
+def test_logits_low_temperature_is_greedy(B, K, V, form):
+    """The low-temperature limit (pinned on the oracle): a greedy draft over
+    integer logits with unique row maxima at tau = 1/64 gives exactly the
+    outputs of greedy verification of the target, at any size; here up to
+    the B=256 K=5 V=128256 shape.  Every rejection's token weight lies
+    below e^-64 of its row's, beyond the fp32 fast test, so the fp64 test
+    decides those rows."""
+    from test_oracle_logits import greedy_limit_instance
+    _case(f"logits tau=1/64 greedy limit B={B} K={K} V={V} form={form}")
+    lp, lq, t, u = greedy_limit_instance(np.random.default_rng(B + K + V), B, K, V)
+    n, nx = run(lp, lq, t, u, 1.0 / 64)
+    am = lp.argmax(axis=2)                                   # the unique maximum of each row
+    miss = np.concatenate([t != am[:, :K], np.ones((B, 1), bool)], axis=1)
+    want_n = miss.argmax(axis=1).astype(np.int32)
+    want_x = am[np.arange(B), want_n].astype(np.int32)
+    assert np.array_equal(n, want_n)
+    assert np.array_equal(nx, want_x)

@@ -13,6 +13,10 @@ requires only that target and draft be warped identically).
    not within 1e-5 of a decision boundary on either side.
 3. Exact invariances of the warp: adding a constant to a row of logits, and
    scaling logits and temperature together, change nothing, bit for bit.
+4. The low-temperature limit: with a greedy draft (each draft token its
+   row's argmax), integer logits whose maximum is unique, tau = 1/64 and
+   uniforms in [1e-6, 1), the outputs are those of greedy verification of
+   the target (the greedy oracle, sv_oracle.c), exactly.
 """
 import numpy as np
 import pytest
@@ -126,3 +130,43 @@ def test_logits_preconditions():
     # all-equal logits: uniform rows, the draft token is accepted (rho = 1 > u)
     r = verify_sample_logits(lp, lq, t, u, 1.0)
     assert r["n_accepted"][0] == 1 and r["next_token"][0] == 0
+
+
+def greedy_limit_instance(rng, B, K, V):
+    """Integer logits in [-20, 20] with one maximum per row, raised 1 above
+    the rest; draft tokens the argmax of their draft row, each row's draft
+    argmax placed at the target's argmax about half the time."""
+    def rows(n):
+        z = rng.integers(-20, 21, size=(B, n, V)).astype(np.float32)
+        top = rng.integers(0, V, size=(B, n))
+        return z, top
+    lp, tp_top = rows(K + 1)
+    lq, tq_top = rows(K)
+    same = rng.random((B, K)) < 0.5
+    tq_top = np.where(same, tp_top[:, :K], tq_top)
+    for z, top in ((lp, tp_top), (lq, tq_top)):
+        bi, ri = np.meshgrid(np.arange(B), np.arange(z.shape[1]), indexing="ij")
+        z[bi, ri, top] = z.max(axis=2) + 1
+    t = tq_top.astype(np.int32)
+    u = rng.uniform(1e-6, 1.0, (B, K + 1)).astype(np.float32)
+    return lp, lq, t, u
+
+
+def test_low_temperature_limit_is_greedy_verification():
+    """At tau = 1/64 every weight but a row's maximum is at most e^-64
+    (logit gap >= 1).  A draft token at the target's argmax has
+    p(t) >= 1 - V e^-64 >= q(t) - V e^-64 and is accepted (u < 1 - 2^-24);
+    one elsewhere has p(t) / q(t) <= e^-64 / (1 - V e^-64) < u and is
+    rejected; the residual and the bonus row put all but V e^-64 of their
+    mass on the target's argmax, which every u in [1e-6, 1 - 2^-24] lands on.
+    So the outputs are greedy verification's, whatever the seed."""
+    rng = np.random.default_rng(64)
+    B, K, V = 300, 4, 700
+    lp, lq, t, u = greedy_limit_instance(rng, B, K, V)
+    r = verify_sample_logits(lp, lq, t, u, 1.0 / 64)
+    w = np.exp(lp.astype(np.float64) - lp.max(axis=2, keepdims=True)).astype(np.float32)
+    g = oracle.verify_greedy(w, t)
+    assert np.array_equal(r["n_accepted"], g["n_accepted"])
+    assert np.array_equal(r["next_token"], g["next_token"])
+    # every outcome occurs
+    assert set(np.unique(g["n_accepted"])) == set(range(K + 1))
