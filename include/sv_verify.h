@@ -136,7 +136,15 @@ sv_status sv_verify_sample_batched(const float* target_probs, const float* draft
  * sv_verify_sample_batched on the warped rows: accept t_i iff
  * u_i * w_q(t_i) * P_i < w_p(t_i) * Q_i, with w(x) = exp((l(x) - max l) / tau)
  * (fp32) and the masses P, Q its fp64 sums; the residual and the draws use
- * the same weights.  One pass over the logits: each chunk publishes its
+ * the same weights.  The two weights of an acceptance test are taken with
+ * fp64 range and an fp64 temperature wherever their exponent leaves
+ * [-16, 0] (in fp32 they could flush to zero at a low temperature).  Every
+ * weight of a row carries one factor 2^e, |e| <= half the fp32 spacing at
+ * |max l| * log2(e) / tau, which cancels; results are specified for
+ * |l| * log2(e) / tau below 2^30 (|e| <= 64), e.g. |l| < 10^4 at
+ * tau >= 10^-4.  Beyond it the sums may overflow or vanish and the outputs
+ * are unspecified (a next_token of -1 included), with no access outside the
+ * arguments.  One pass over the logits: each chunk publishes its
  * maximum and its weight sum against it, and readers rescale to the row's
  * maximum.  No row statistics.  The workspace is that of the sampled call
  * (sv_workspace_size(B, K, V, 1)).  One launch on `stream`.

@@ -238,3 +238,17 @@ def test_logits_low_temperature_is_greedy(B, K, V, form):
     want_x = am[np.arange(B), want_n].astype(np.int32)
     assert np.array_equal(n, want_n)
     assert np.array_equal(nx, want_x)
+
+
+@pytest.mark.parametrize("B,K,V", [(4, 3, 5000), (2, 5, 40001)], ids=lambda x: str(x))
+def test_logits_large_offsets(B, K, V, form):
+    """Logits far from 0 (target +1e5, draft -3e4, each row its own extra
+    offset) at tau = 0.5: the fp32 rounding of max l * log2(e) / tau is then
+    2^-5 or so and scales every weight of a row alike, so it must cancel;
+    the outputs equal the oracle's on the same f32 logits."""
+    _case(f"logits large offsets B={B} K={K} V={V} form={form}")
+    rng = np.random.default_rng(B * 7 + K + V)
+    lp, lq, t, u = _rows(rng, B, K, V, 0.5)
+    lp = (lp + np.float32(1e5) + rng.uniform(-500, 500, (B, K + 1, 1)).astype(np.float32)).astype(np.float32)
+    lq = (lq - np.float32(3e4) + rng.uniform(-500, 500, (B, K, 1)).astype(np.float32)).astype(np.float32)
+    check(*run(lp, lq, t, u, 0.5), verify_sample_logits(lp, lq, t, u, 0.5))

@@ -271,6 +271,28 @@ def test_edge_out_of_range_tokens_and_one_hot(form):
     check_greedy(gn, gx, gst, oracle.verify_greedy(p, t))
 
 
+def test_edge_extreme_scales(form):
+    """The method is scale-free (the test compares u q(t) P with p(t) Q, the
+    residual is p Q - q P): rows scaled far from 1 decide as the oracle does
+    on the same f32 values.  Subnormal rows (every value below 2^-126, so
+    the loads, maxima and sums see subnormal f32), rows near 2^110, and a
+    target and draft 2^200 apart; statistics to the usual bar."""
+    _case(f"edge: extreme scales (subnormal to 2^110), form={form}")
+    rng = np.random.default_rng(23)
+    B, K, V = 8, 3, 9000
+    p, q, t, u = _random_rows(rng, B, K, V, ties=True)
+    scales = [(2.0**-140, 2.0**-140), (2.0**100, 2.0**-100), (2.0**-130, 1.0), (2.0**110, 2.0**110),
+              (1.0, 2.0**-135), (2.0**-100, 2.0**100)]
+    for b, (sp, sq) in enumerate(scales):
+        p[b] *= np.float32(sp)
+        q[b] *= np.float32(sq)
+    assert p[0].max() < np.finfo(np.float32).tiny and p[0].max() > 0 and np.isfinite(p).all()
+    n, nx, st = run_sample(p, q, t, u)
+    check_sampled(n, nx, st, oracle.verify_sample(p, q, t, u))
+    gn, gx, gst = run_greedy(p, t)
+    check_greedy(gn, gx, gst, oracle.verify_greedy(p, t))
+
+
 def test_edge_all_equal_rows_tie_to_index_zero():
     _case("edge: constant rows")
     B, K, V = 3, 2, 20000
