@@ -4,8 +4,11 @@ against the fp64 logits oracle (oracle/logits.py), through the C ABI.
 The bar is that of the sampled path: n_accepted and next_token identical on
 every sequence whose decisions all lie more than 1e-5 of their mass from a
 boundary (the oracle's margins); boundary sequences are counted.  The kernel
-warps each value in fp32 (exp2 of an fp32 argument), so its weights differ
-from the oracle's fp64 exp by ~1e-7 relative: far inside that band.
+warps each value in fp32 (exp2 of an fp32 argument), so its weights near a
+row's maximum differ from the oracle's fp64 exp by ~1e-7 relative: far
+inside that band.  An acceptance test's two weights, whose exponents can be
+far below fp32's range at a low temperature, are taken with fp64 range
+(the extreme-temperature and low-temperature-limit cases reach that path).
 """
 import os
 
