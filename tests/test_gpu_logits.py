@@ -255,3 +255,27 @@ def test_logits_large_offsets(B, K, V, form):
     lp = (lp + np.float32(1e5) + rng.uniform(-500, 500, (B, K + 1, 1)).astype(np.float32)).astype(np.float32)
     lq = (lq - np.float32(3e4) + rng.uniform(-500, 500, (B, K, 1)).astype(np.float32)).astype(np.float32)
     check(*run(lp, lq, t, u, 0.5), verify_sample_logits(lp, lq, t, u, 0.5))
+
+
+def test_logits_underflowing_token_weights(form):
+    """Draft tokens whose warped weights both lie far below fp32's range at
+    tau = 0.02 (exponents near -650 and -720): row 0 of sequence 0 has the
+    token 9 below the target row's maximum and 10 below the draft row's, a
+    ratio p(t)/q(t) of 2^72, and must be accepted; sequence 1 mirrors it
+    (ratio 2^-72) and must be rejected.  In fp32 both weights would be 0 and
+    the test 0 < 0 would reject both."""
+    _case(f"logits underflowing token weights tau=0.02 form={form}")
+    B, K, V, tau = 2, 2, 5000, 0.02
+    rng = np.random.default_rng(77)
+    lp = rng.normal(0.0, 2.0, (B, K + 1, V)).astype(np.float32)
+    lq = rng.normal(0.0, 2.0, (B, K, V)).astype(np.float32)
+    t = np.array([[17, 4001], [17, 4001]], np.int32)
+    for b, (gp, gq) in enumerate([(9.0, 10.0), (10.0, 9.0)]):
+        lp[b, 0, 17] = lp[b, 0].max() - np.float32(gp)
+        lq[b, 0, 17] = lq[b, 0].max() - np.float32(gq)
+    u = np.full((B, K + 1), 0.5, np.float32)
+    o = verify_sample_logits(lp, lq, t, u, tau)
+    assert o["n_accepted"][0] >= 1 and o["n_accepted"][1] == 0
+    n, nx = run(lp, lq, t, u, tau)
+    check(n, nx, o)
+    assert n[0] >= 1 and n[1] == 0
