@@ -118,6 +118,9 @@ def main():
     ap.add_argument("--logits", action="store_true",
                     help="sampled verification given logits (warped in the library) instead of probabilities")
     ap.add_argument("--temperature", type=float, default=1.0, help="temperature of --logits")
+    ap.add_argument("--early-exit", action="store_true",
+                    help="sampled verification through the early-exit entry point (reads only the rows the "
+                         "outputs depend on; its byte count is those rows)")
     ap.add_argument("--decoder", action="store_true",
                     help="time rounds of the multi-round driver (B=1, K=4, V=32000) instead")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -149,9 +152,13 @@ def main():
             raise SystemExit("--logits takes workload 1 or 3 (families with logits)")
         mode = "sampled"
     sampled = mode == "sampled"
+    if args.early_exit and (args.logits or not sampled):
+        raise SystemExit("--early-exit takes the sampled mode on probabilities")
     B, K, V = cfg["B"], cfg["K"], cfg["V"]
     dev = torch.device("cuda:0")
     workload = f"B={B} K={K} V={V} {mode}" + (f" logits tau={args.temperature:g}" if args.logits else "")
+    if args.early_exit:
+        workload += " early-exit"
     log(f"workload {args.workload}: {workload}; generating {args.sets} input sets")
 
     sets = []
@@ -168,6 +175,9 @@ def main():
         if args.logits:
             sv.sv_verify_sample_logits_batched(db["tp"], db["dp"], db["dt"], db["u"], args.temperature,
                                                n_accepted=n_out, next_token=x_out, workspace=ws, stream=stream)
+        elif args.early_exit:
+            sv.sv_verify_sample_early_batched(db["tp"], db["dp"], db["dt"], db["u"], n_accepted=n_out,
+                                              next_token=x_out, workspace=ws, stream=stream)
         elif sampled:
             sv.sv_verify_sample_batched(db["tp"], db["dp"], db["dt"], db["u"], n_accepted=n_out,
                                         next_token=x_out, workspace=ws, stream=stream)
@@ -202,6 +212,17 @@ def main():
                       logits=args.logits, tau=args.temperature)
 
     fbytes = workloads.formula_bytes(B, K, V, sampled)
+    formula = fbytes
+    if args.early_exit:
+        # the early exit's algorithmic bytes: the rows the outputs depend on
+        # (pairs 0..n, and row K after full acceptance), averaged over the
+        # input sets, which the timed steps use equally often
+        need = []
+        for db in sets:
+            step(db)
+            n = n_out.cpu().numpy().astype(np.int64)
+            need.append(int(((np.where(n < K, 2 * (n + 1), 2 * K + 1)) * V * 4).sum()))
+        fbytes = int(round(sum(need) / len(need)))
     achieved = fbytes / (avg_ms * 1e-3) / 1e9
     kernel = "sv_logits_kernel" if args.logits else ("sv_sample_kernel" if sampled else "sv_greedy_kernel")
     rounds_per_s = args.steps / wall
@@ -227,6 +248,7 @@ def main():
                      "traffic": traffic_for(kernel, workload),
                      "kernel": kernel, "kernel_avg_us": round(avg_ms * 1e3, 2),
                      "algorithmic_bytes_per_launch": fbytes},
+        **({"formula_bytes_per_launch": formula} if args.early_exit else {}),
         "accumulation": "f64",
         "parity_spot": spot,
         "context": {"pages_cpu_latency_us": {"greedy": 33, "sampled": 117,

@@ -128,6 +128,23 @@ sv_status sv_verify_sample_batched(const float* target_probs, const float* draft
                                    void* workspace, size_t workspace_bytes,
                                    sv_row_stats* stats, void* stream);
 
+/* Sampled verification with an early exit: the outputs of
+ * sv_verify_sample_batched, bit for bit (the same decisions from the same
+ * partial sums), reading only what they depend on (the card's sequential
+ * rule, section "Method", stops at the first rejected draft).  A sequence's
+ * walks stop after its first rejected row n (the row after n is already in
+ * flight), and the bonus row's blocks skip their loads once that rejection
+ * is published.  So a batch reads about the pairs 0..n+1 of each sequence,
+ * plus row K after full acceptance, not the whole operands.  Same arguments,
+ * workspace and errors as sv_verify_sample_batched, without row statistics
+ * (they need every row).  Small grids that take one block per draft row read
+ * every row as before. */
+sv_status sv_verify_sample_early_batched(const float* target_probs, const float* draft_probs,
+                                         const int32_t* draft_tokens, const float* uniforms,
+                                         int32_t B, int32_t K, int32_t V,
+                                         int32_t* n_accepted, int32_t* next_token,
+                                         void* workspace, size_t workspace_bytes, void* stream);
+
 /* Sampled verification on logits, warped by one temperature (the card's
  * speculative-sampling bullet holds when target and draft are warped
  * identically; here the library warps both).  target_logits [B, K+1, V] and

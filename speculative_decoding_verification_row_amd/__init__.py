@@ -33,7 +33,8 @@ import torch
 __all__ = [
     "SVError", "ROW_STATS_DTYPE", "library_path", "load_library",
     "sv_workspace_size", "sv_workspace_init", "sv_workspace_error", "sv_status_string",
-    "sv_verify_greedy_batched", "sv_verify_sample_batched", "sv_verify_sample_logits_batched",
+    "sv_verify_greedy_batched", "sv_verify_sample_batched", "sv_verify_sample_early_batched",
+    "sv_verify_sample_logits_batched",
     "verify_greedy", "verify_sample", "stats_to_numpy", "workspace_for",
     "SpeculativeDecoder", "DecodeStats", "Governor",
 ]
@@ -85,6 +86,8 @@ def load_library():
     lib.sv_verify_greedy_batched.restype = ctypes.c_int
     lib.sv_verify_sample_batched.argtypes = [P, P, P, P, I32, I32, I32, P, P, P, SZ, P, P]
     lib.sv_verify_sample_batched.restype = ctypes.c_int
+    lib.sv_verify_sample_early_batched.argtypes = [P, P, P, P, I32, I32, I32, P, P, P, SZ, P]
+    lib.sv_verify_sample_early_batched.restype = ctypes.c_int
     lib.sv_verify_sample_logits_batched.argtypes = [P, P, P, P, ctypes.c_float, I32, I32, I32, P, P, P, SZ, P]
     lib.sv_verify_sample_logits_batched.restype = ctypes.c_int
     lib.sv_workspace_error.argtypes = [P, ctypes.POINTER(I32), P]
@@ -280,6 +283,33 @@ def sv_verify_sample_batched(target_probs: torch.Tensor, draft_probs: torch.Tens
     if rc != SV_OK:
         raise SVError(rc, "sv_verify_sample_batched")
     return (n_accepted, next_token, st) if st is not None else (n_accepted, next_token)
+
+
+def sv_verify_sample_early_batched(target_probs: torch.Tensor, draft_probs: torch.Tensor,
+                                   draft_tokens: torch.Tensor, uniforms: torch.Tensor,
+                                   n_accepted=None, next_token=None, workspace=None, stream=None):
+    """Sampled verification with an early exit: the outputs of
+    sv_verify_sample_batched bit for bit, reading only the rows they depend
+    on (about the pairs 0..n+1 of each sequence, and row K after full
+    acceptance).  No row statistics.  Returns (n_accepted, next_token)."""
+    B, K1, V = target_probs.shape
+    K = K1 - 1
+    dev = _device_of(target_probs, "target_probs")
+    _check(target_probs, "target_probs", torch.float32, (B, K1, V), dev)
+    _check(draft_probs, "draft_probs", torch.float32, (B, K, V), dev)
+    _check(draft_tokens, "draft_tokens", torch.int32, (B, K), dev)
+    _check(uniforms, "uniforms", torch.float32, (B, K1), dev)
+    n_accepted, next_token = _outputs(B, dev, n_accepted, next_token)
+    if workspace is None:
+        workspace = workspace_for(B, K, V, True, dev, stream)
+    _check_workspace(workspace, dev)
+    rc = _call(dev, load_library().sv_verify_sample_early_batched,
+               target_probs.data_ptr(), draft_probs.data_ptr(), draft_tokens.data_ptr(), uniforms.data_ptr(),
+               B, K, V, n_accepted.data_ptr(), next_token.data_ptr(),
+               workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream_handle(stream, dev))
+    if rc != SV_OK:
+        raise SVError(rc, "sv_verify_sample_early_batched")
+    return n_accepted, next_token
 
 
 def sv_verify_sample_logits_batched(target_logits: torch.Tensor, draft_logits: torch.Tensor,

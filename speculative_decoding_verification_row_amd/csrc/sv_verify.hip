@@ -134,6 +134,7 @@ struct Args {
     unsigned long long poll_ticks;   // wait bound in wall-clock ticks
     float ktau;                      // logits: log2(e) / temperature
     double ktau64;                   // the same in fp64 (acceptance weights)
+    int early;                       // sampled: read no row a decided sequence no longer needs
 };
 
 // ------------------------------------------- cross-block communication --
@@ -1258,6 +1259,20 @@ __global__ __launch_bounds__(kThreads, 4) void sv_sample_kernel(Args a)
         const int b = (int)(blk / (unsigned)per_seq);
         const int c0 = (int)(blk - (unsigned)b * (unsigned)per_seq) * kBonusChunks;
         const int64_t row0 = (int64_t)b * (K + 1);
+        if (!ROWS && a.early && K > 0) {
+            // Early exit: the bonus row is needed only after full acceptance.
+            // Once the walks' outcome shows a rejection (they published it
+            // when they ended, normally long before this block runs), nothing
+            // reads this row.  Without the outcome the row is read as always.
+            __shared__ int s_skip;
+            if (threadIdx.x == 0) {
+                const unsigned long long v = get_u64(&a.sstate[b]);
+                const unsigned long long code = v >> 8;
+                s_skip = f64_ok(v, a.epoch) && !a.force_recompute && code >= 1 && code <= (unsigned long long)K;
+            }
+            __syncthreads();
+            if (s_skip) return;
+        }
         const Row prow = row_of(a.tp + (row0 + K) * V, V);
         float4 xp[kBonusChunks][kVecS];
 #pragma unroll
@@ -1375,6 +1390,11 @@ __global__ __launch_bounds__(kThreads, 4) void sv_sample_kernel(Args a)
             break;
         }
     }
+    // Early exit: after a decided rejection no later row is read.  Every
+    // reader of this sequence needs rows 0..n only (the decisions, the
+    // residual of row n); the row after n is already in flight.  A walk
+    // that lost its decision still publishes every row, for the finisher.
+    if (a.early && state >= 0) i = K;
     for (; i < K; ++i) {   // after the first rejection (or a lost decision)
         load_next(i);
         __builtin_amdgcn_sched_barrier(0);
@@ -2491,6 +2511,16 @@ Args make_args(void* ws, int32_t B, int32_t K, int32_t V, bool sampled)
 
 }  // namespace
 
+namespace {
+// The body of both sampled entry points (early: the early-exit form).
+sv_status sample_call(const float* target_probs, const float* draft_probs,
+                      const int32_t* draft_tokens, const float* uniforms,
+                      int32_t B, int32_t K, int32_t V,
+                      int32_t* n_accepted, int32_t* next_token,
+                      void* workspace, size_t workspace_bytes,
+                      sv_row_stats* stats, void* stream, bool early);
+}   // namespace
+
 extern "C" {
 
 size_t sv_workspace_size(int32_t B, int32_t K, int32_t V, int32_t sampled)
@@ -2564,6 +2594,29 @@ sv_status sv_verify_sample_batched(const float* target_probs, const float* draft
                                    void* workspace, size_t workspace_bytes,
                                    sv_row_stats* stats, void* stream)
 {
+    return sample_call(target_probs, draft_probs, draft_tokens, uniforms, B, K, V, n_accepted, next_token,
+                       workspace, workspace_bytes, stats, stream, false);
+}
+
+sv_status sv_verify_sample_early_batched(const float* target_probs, const float* draft_probs,
+                                         const int32_t* draft_tokens, const float* uniforms,
+                                         int32_t B, int32_t K, int32_t V,
+                                         int32_t* n_accepted, int32_t* next_token,
+                                         void* workspace, size_t workspace_bytes, void* stream)
+{
+    return sample_call(target_probs, draft_probs, draft_tokens, uniforms, B, K, V, n_accepted, next_token,
+                       workspace, workspace_bytes, nullptr, stream, true);
+}
+}   // extern "C"
+
+namespace {
+sv_status sample_call(const float* target_probs, const float* draft_probs,
+                      const int32_t* draft_tokens, const float* uniforms,
+                      int32_t B, int32_t K, int32_t V,
+                      int32_t* n_accepted, int32_t* next_token,
+                      void* workspace, size_t workspace_bytes,
+                      sv_row_stats* stats, void* stream, bool early)
+{
     sv_status st = check_sizes(B, K, V);
     if (st != SV_OK) return st;
     if (B == 0) return SV_OK;   // nothing to verify; pointers are not inspected
@@ -2590,6 +2643,7 @@ sv_status sv_verify_sample_batched(const float* target_probs, const float* draft
     a.n_out = n_accepted;
     a.next_out = next_token;
     a.stats = stats;
+    a.early = early ? 1 : 0;
     const Tuning tu = tuning();
     a.force_recompute = tu.force_recompute;
     a.poll_ticks = (unsigned long long)(tu.poll_us * 1e-3 * (double)d.wall_khz);
@@ -2609,6 +2663,9 @@ sv_status sv_verify_sample_batched(const float* target_probs, const float* draft
         launch_sample<false, false>(rows, grid, s, a);
     return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
+}   // namespace
+
+extern "C" {
 
 sv_status sv_verify_sample_logits_batched(const float* target_logits, const float* draft_logits,
                                           const int32_t* draft_tokens, const float* uniforms, float temperature,

@@ -119,6 +119,21 @@ def test_argument_errors_sampled(lib):
     assert _sample(lib, B=0) == 0
 
 
+def test_argument_errors_sampled_early(lib):
+    def early(tp=FAKE, dp=FAKE, dt=FAKE, u=FAKE, B=1, K=1, V=8, wsb=1 << 20, ws=FAKE):
+        return lib.sv_verify_sample_early_batched(tp, dp, dt, u, B, K, V, FAKE, FAKE, ws, wsb, None)
+    assert early(tp=None) == -1
+    assert early(dp=None) == -1
+    assert early(u=None) == -1
+    assert early(B=-3) == -1
+    assert early(u=ctypes.c_void_p(0x10001)) == -1
+    assert early(V=600000) == -4
+    assert early(wsb=0) == -2
+    assert early(ws=ctypes.c_void_p(0x10008)) == -2
+    assert early(dp=None, dt=None, K=0, B=0) == 0
+    assert early(B=0) == 0
+
+
 def test_binding_without_library_fails_loudly(monkeypatch, tmp_path):
     import speculative_decoding_verification_row_amd as sv
     monkeypatch.setattr(sv, "_lib", None)
