@@ -132,9 +132,9 @@ sv_status sv_verify_sample_batched(const float* target_probs, const float* draft
  * sv_verify_sample_batched, bit for bit (the same decisions from the same
  * partial sums), reading only what they depend on (the card's sequential
  * rule, section "Method", stops at the first rejected draft).  A sequence's
- * walks stop after its first rejected row n (the row after n is already in
- * flight), and the bonus row's blocks skip their loads once that rejection
- * is published.  So a batch reads about the pairs 0..n+1 of each sequence,
+ * walks issue a row's loads only once the row two before it is accepted, so
+ * they stop after the pairs 0..n+1 for a first rejection at n, and the bonus
+ * row's blocks skip their loads once that rejection is published.  So a batch reads about the pairs 0..n+1 of each sequence,
  * plus row K after full acceptance, not the whole operands.  Same arguments,
  * workspace and errors as sv_verify_sample_batched, without row statistics
  * (they need every row).  Small grids that take one block per draft row read

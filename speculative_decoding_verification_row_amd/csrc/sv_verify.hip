@@ -1242,7 +1242,7 @@ __device__ __noinline__ void finish_bonus_call(const Args& a, int b)
     finish_bonus<VEC, STATS, ROWS>(a, b);
 }
 
-template <bool VEC, bool STATS, bool ROWS>
+template <bool VEC, bool STATS, bool ROWS, bool EARLY = false>
 __global__ __launch_bounds__(kThreads, 4) void sv_sample_kernel(Args a)
 {
     constexpr int MP = STATS ? (kSP | kSQ | kSMIN | kAM) : (kSP | kSQ);   // rows 0..K-1
@@ -1375,10 +1375,13 @@ __global__ __launch_bounds__(kThreads, 4) void sv_sample_kernel(Args a)
         if (pending) pl = poll_issue(a, b, i - 1, tok);
         if (threadIdx.x == 0) tok = a.dt[(int64_t)b * K + i];   // row i's token, for step i+1
         __builtin_amdgcn_sched_barrier(0);
-        load_next(i);
+        if (!EARLY) load_next(i);
         __builtin_amdgcn_sched_barrier(0);
         publish_part<MP>(a, row0 + i, c, block_reduce<MP, false>(thread_stats<MP, kVecS>(xp, xq, c), i & 1));
         if (pending) decide(i - 1, pl);
+        // the early exit issues row i+1's loads only once row i-1 is
+        // accepted, so that a rejection at n leaves rows n+2.. unread
+        if (EARLY && state == kSearching) load_next(i);
         if (state == kSearching) park(xp, xq);
 #pragma unroll
         for (int k = 0; k < kVecS; ++k) {
@@ -1394,7 +1397,7 @@ __global__ __launch_bounds__(kThreads, 4) void sv_sample_kernel(Args a)
     // reader of this sequence needs rows 0..n only (the decisions, the
     // residual of row n); the row after n is already in flight.  A walk
     // that lost its decision still publishes every row, for the finisher.
-    if (a.early && state >= 0) i = K;
+    if (EARLY && state >= 0) i = K;
     for (; i < K; ++i) {   // after the first rejection (or a lost decision)
         load_next(i);
         __builtin_amdgcn_sched_barrier(0);
@@ -2437,6 +2440,8 @@ void launch_sample(bool rows, dim3 grid, hipStream_t s, const Args& a)
 {
     if (rows)
         hipLaunchKernelGGL((sv_sample_kernel<VEC, STATS, true>), grid, dim3(kThreads), 0, s, a);
+    else if (!STATS && a.early)
+        hipLaunchKernelGGL((sv_sample_kernel<VEC, false, false, true>), grid, dim3(kThreads), 0, s, a);
     else
         hipLaunchKernelGGL((sv_sample_kernel<VEC, STATS, false>), grid, dim3(kThreads), 0, s, a);
 }
