@@ -152,8 +152,8 @@ def main():
             raise SystemExit("--logits takes workload 1 or 3 (families with logits)")
         mode = "sampled"
     sampled = mode == "sampled"
-    if args.early_exit and (args.logits or not sampled):
-        raise SystemExit("--early-exit takes the sampled mode on probabilities")
+    if args.early_exit and not sampled:
+        raise SystemExit("--early-exit takes the sampled mode (probabilities or --logits)")
     B, K, V = cfg["B"], cfg["K"], cfg["V"]
     dev = torch.device("cuda:0")
     workload = f"B={B} K={K} V={V} {mode}" + (f" logits tau={args.temperature:g}" if args.logits else "")
@@ -173,8 +173,9 @@ def main():
 
     def step(db):
         if args.logits:
-            sv.sv_verify_sample_logits_batched(db["tp"], db["dp"], db["dt"], db["u"], args.temperature,
-                                               n_accepted=n_out, next_token=x_out, workspace=ws, stream=stream)
+            f = sv.sv_verify_sample_logits_early_batched if args.early_exit else sv.sv_verify_sample_logits_batched
+            f(db["tp"], db["dp"], db["dt"], db["u"], args.temperature,
+              n_accepted=n_out, next_token=x_out, workspace=ws, stream=stream)
         elif args.early_exit:
             sv.sv_verify_sample_early_batched(db["tp"], db["dp"], db["dt"], db["u"], n_accepted=n_out,
                                               next_token=x_out, workspace=ws, stream=stream)

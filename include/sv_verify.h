@@ -173,6 +173,16 @@ sv_status sv_verify_sample_logits_batched(const float* target_logits, const floa
                                           int32_t* n_accepted, int32_t* next_token,
                                           void* workspace, size_t workspace_bytes, void* stream);
 
+/* Sampled verification on logits with an early exit: the outputs of
+ * sv_verify_sample_logits_batched, bit for bit, reading only what they
+ * depend on, as sv_verify_sample_early_batched does for probabilities.
+ * Same arguments, workspace and errors as sv_verify_sample_logits_batched. */
+sv_status sv_verify_sample_logits_early_batched(const float* target_logits, const float* draft_logits,
+                                                const int32_t* draft_tokens, const float* uniforms,
+                                                float temperature, int32_t B, int32_t K, int32_t V,
+                                                int32_t* n_accepted, int32_t* next_token,
+                                                void* workspace, size_t workspace_bytes, void* stream);
+
 /* Synchronously read the workspace's device-fault word into *error_out
  * (host memory), waiting for `stream` first: 0 when every call since the
  * last sv_workspace_init completed normally.  The current kernels never set

@@ -34,7 +34,7 @@ __all__ = [
     "SVError", "ROW_STATS_DTYPE", "library_path", "load_library",
     "sv_workspace_size", "sv_workspace_init", "sv_workspace_error", "sv_status_string",
     "sv_verify_greedy_batched", "sv_verify_sample_batched", "sv_verify_sample_early_batched",
-    "sv_verify_sample_logits_batched",
+    "sv_verify_sample_logits_batched", "sv_verify_sample_logits_early_batched",
     "verify_greedy", "verify_sample", "stats_to_numpy", "workspace_for",
     "SpeculativeDecoder", "DecodeStats", "Governor",
 ]
@@ -90,6 +90,8 @@ def load_library():
     lib.sv_verify_sample_early_batched.restype = ctypes.c_int
     lib.sv_verify_sample_logits_batched.argtypes = [P, P, P, P, ctypes.c_float, I32, I32, I32, P, P, P, SZ, P]
     lib.sv_verify_sample_logits_batched.restype = ctypes.c_int
+    lib.sv_verify_sample_logits_early_batched.argtypes = [P, P, P, P, ctypes.c_float, I32, I32, I32, P, P, P, SZ, P]
+    lib.sv_verify_sample_logits_early_batched.restype = ctypes.c_int
     lib.sv_workspace_error.argtypes = [P, ctypes.POINTER(I32), P]
     lib.sv_workspace_error.restype = ctypes.c_int
     lib.sv_status_string.argtypes = [ctypes.c_int]
@@ -340,6 +342,31 @@ def sv_verify_sample_logits_batched(target_logits: torch.Tensor, draft_logits: t
         raise SVError(rc, "sv_verify_sample_logits_batched")
     return n_accepted, next_token
 
+
+def sv_verify_sample_logits_early_batched(target_logits: torch.Tensor, draft_logits: torch.Tensor,
+                                    draft_tokens: torch.Tensor, uniforms: torch.Tensor, temperature: float,
+                                    n_accepted=None, next_token=None, workspace=None, stream=None):
+    """Sampled verification on logits with an early exit: the outputs of
+    sv_verify_sample_logits_batched bit for bit, reading only the rows they
+    depend on.  Same arguments."""
+    B, K1, V = target_logits.shape
+    K = K1 - 1
+    dev = _device_of(target_logits, "target_logits")
+    _check(target_logits, "target_logits", torch.float32, (B, K1, V), dev)
+    _check(draft_logits, "draft_logits", torch.float32, (B, K, V), dev)
+    _check(draft_tokens, "draft_tokens", torch.int32, (B, K), dev)
+    _check(uniforms, "uniforms", torch.float32, (B, K1), dev)
+    n_accepted, next_token = _outputs(B, dev, n_accepted, next_token)
+    if workspace is None:
+        workspace = workspace_for(B, K, V, True, dev, stream)
+    _check_workspace(workspace, dev)
+    rc = _call(dev, load_library().sv_verify_sample_logits_early_batched,
+               target_logits.data_ptr(), draft_logits.data_ptr(), draft_tokens.data_ptr(), uniforms.data_ptr(),
+               float(temperature), B, K, V, n_accepted.data_ptr(), next_token.data_ptr(),
+               workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream_handle(stream, dev))
+    if rc != SV_OK:
+        raise SVError(rc, "sv_verify_sample_logits_early_batched")
+    return n_accepted, next_token
 
 def stats_to_numpy(stats: torch.Tensor) -> np.ndarray:
     """[B, K+1, 48] uint8 device tensor -> [B, K+1] ROW_STATS_DTYPE array."""

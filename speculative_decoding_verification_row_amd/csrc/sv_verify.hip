@@ -2172,7 +2172,7 @@ __device__ int wait_state_l(const Args& a, int b)
     return code;
 }
 
-template <bool VEC, bool ROWS>
+template <bool VEC, bool ROWS, bool EARLY = false>
 __global__ __launch_bounds__(kThreads, 4) void sv_logits_kernel(Args a)
 {
     const int NC = a.NC, K = a.K, V = a.V;
@@ -2191,6 +2191,18 @@ __global__ __launch_bounds__(kThreads, 4) void sv_logits_kernel(Args a)
         b = (int)(blk / (unsigned)per_seq);
         const int c0 = (int)(blk - (unsigned)b * (unsigned)per_seq) * kBonusChunks;
         const int64_t row0 = (int64_t)b * (K + 1);
+        if (EARLY && K > 0) {
+            // early exit: skip the bonus row once the walks' outcome shows a
+            // rejection (as in sv_sample_kernel)
+            __shared__ int s_skip;
+            if (threadIdx.x == 0) {
+                const unsigned long long v = get_u64(&a.sstate[b]);
+                const unsigned long long code = v >> 8;
+                s_skip = f64_ok(v, a.epoch) && !a.force_recompute && code >= 1 && code <= (unsigned long long)K;
+            }
+            __syncthreads();
+            if (s_skip) return;
+        }
         const Row prow = row_of(a.tp + (row0 + K) * V, V);
         float4 xp[kBonusChunks][kVecS];
 #pragma unroll
@@ -2287,10 +2299,11 @@ __global__ __launch_bounds__(kThreads, 4) void sv_logits_kernel(Args a)
         if (pending) pl = poll_issue_l(a, b, i - 1, tok);
         if (threadIdx.x == 0) tok = a.dt[(int64_t)b * K + i];
         __builtin_amdgcn_sched_barrier(0);
-        load_next(i);
+        if (!EARLY) load_next(i);
         __builtin_amdgcn_sched_barrier(0);
         publish_l(a, row0 + i, c, chunk_stats_l<kVecS, true>(xp, xq, c, V, kt, i & 1), true);
         if (pending) decide(i - 1, pl);
+        if (EARLY && state == kSearching) load_next(i);   // early exit: loads after the decision
         if (state == kSearching) park(xp, xq);
 #pragma unroll
         for (int j = 0; j < kVecS; ++j) {
@@ -2302,6 +2315,7 @@ __global__ __launch_bounds__(kThreads, 4) void sv_logits_kernel(Args a)
             break;
         }
     }
+    if (EARLY && state >= 0) i = K;   // early exit: no row after a decided rejection
     for (; i < K; ++i) {
         load_next(i);
         __builtin_amdgcn_sched_barrier(0);
@@ -2524,6 +2538,12 @@ sv_status sample_call(const float* target_probs, const float* draft_probs,
                       int32_t* n_accepted, int32_t* next_token,
                       void* workspace, size_t workspace_bytes,
                       sv_row_stats* stats, void* stream, bool early);
+// The body of both logits entry points.
+sv_status logits_call(const float* target_logits, const float* draft_logits,
+                      const int32_t* draft_tokens, const float* uniforms, float temperature,
+                      int32_t B, int32_t K, int32_t V,
+                      int32_t* n_accepted, int32_t* next_token,
+                      void* workspace, size_t workspace_bytes, void* stream, bool early);
 }   // namespace
 
 extern "C" {
@@ -2678,6 +2698,28 @@ sv_status sv_verify_sample_logits_batched(const float* target_logits, const floa
                                           int32_t* n_accepted, int32_t* next_token,
                                           void* workspace, size_t workspace_bytes, void* stream)
 {
+    return logits_call(target_logits, draft_logits, draft_tokens, uniforms, temperature, B, K, V, n_accepted,
+                       next_token, workspace, workspace_bytes, stream, false);
+}
+
+sv_status sv_verify_sample_logits_early_batched(const float* target_logits, const float* draft_logits,
+                                                const int32_t* draft_tokens, const float* uniforms,
+                                                float temperature, int32_t B, int32_t K, int32_t V,
+                                                int32_t* n_accepted, int32_t* next_token,
+                                                void* workspace, size_t workspace_bytes, void* stream)
+{
+    return logits_call(target_logits, draft_logits, draft_tokens, uniforms, temperature, B, K, V, n_accepted,
+                       next_token, workspace, workspace_bytes, stream, true);
+}
+}   // extern "C"
+
+namespace {
+sv_status logits_call(const float* target_logits, const float* draft_logits,
+                      const int32_t* draft_tokens, const float* uniforms, float temperature,
+                      int32_t B, int32_t K, int32_t V,
+                      int32_t* n_accepted, int32_t* next_token,
+                      void* workspace, size_t workspace_bytes, void* stream, bool early)
+{
     sv_status st = check_sizes(B, K, V);
     if (st != SV_OK) return st;
     if (!(std::isfinite(temperature) && temperature > 0.0f)) return SV_ERR_INVALID_ARG;
@@ -2715,16 +2757,24 @@ sv_status sv_verify_sample_logits_batched(const float* target_logits, const floa
     const bool rows = use_rows(K, per_row, bonus, kRowsBlocksPerRowL, tu);
     a.nwalk = (unsigned)(K > 0 ? (rows ? (uint64_t)K * per_row : per_row) : 0);
     const dim3 grid((unsigned)(a.nwalk + bonus)), block(kThreads);
+    a.early = early ? 1 : 0;
     if (vec && rows)
         hipLaunchKernelGGL((sv_logits_kernel<true, true>), grid, block, 0, s, a);
+    else if (vec && early)
+        hipLaunchKernelGGL((sv_logits_kernel<true, false, true>), grid, block, 0, s, a);
     else if (vec)
         hipLaunchKernelGGL((sv_logits_kernel<true, false>), grid, block, 0, s, a);
     else if (rows)
         hipLaunchKernelGGL((sv_logits_kernel<false, true>), grid, block, 0, s, a);
+    else if (early)
+        hipLaunchKernelGGL((sv_logits_kernel<false, false, true>), grid, block, 0, s, a);
     else
         hipLaunchKernelGGL((sv_logits_kernel<false, false>), grid, block, 0, s, a);
     return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
+}   // namespace
+
+extern "C" {
 
 sv_status sv_workspace_error(const void* workspace, int32_t* error_out, void* stream)
 {

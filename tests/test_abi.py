@@ -132,6 +132,15 @@ def test_argument_errors_sampled_early(lib):
     assert early(ws=ctypes.c_void_p(0x10008)) == -2
     assert early(dp=None, dt=None, K=0, B=0) == 0
     assert early(B=0) == 0
+    # the logits form: the same checks, and a temperature that is finite and > 0
+    def early_l(tau=1.0, tp=FAKE, B=1, K=1, V=8, wsb=1 << 20):
+        return lib.sv_verify_sample_logits_early_batched(tp, FAKE, FAKE, FAKE, tau, B, K, V, FAKE, FAKE, FAKE,
+                                                         wsb, None)
+    assert early_l(tp=None) == -1
+    assert early_l(tau=0.0) == -1
+    assert early_l(tau=float("nan")) == -1
+    assert early_l(wsb=0) == -2
+    assert early_l(B=0) == 0
 
 
 def test_binding_without_library_fails_loudly(monkeypatch, tmp_path):

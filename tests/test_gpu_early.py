@@ -108,3 +108,46 @@ def test_early_full_workload():
     assert sv.sv_workspace_error(ws) == 0
     del sets
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("tau", [0.5, 1.0, 0.02])
+@pytest.mark.parametrize("B,K,V", [(5, 4, 1000), (3, 3, 1003), (2, 5, 40001), (3, 9, 5000)],
+                         ids=lambda x: str(x))
+def test_early_logits(B, K, V, tau, form):
+    """The logits early exit: outputs equal to the full logits pass's, bit
+    for bit, and to the logits oracle's to the sampled bar."""
+    from test_gpu_logits import _rows as logit_rows, check
+    from oracle.logits import verify_sample_logits
+    _case(f"early exit logits B={B} K={K} V={V} tau={tau} form={form}")
+    lp, lq, t, u = logit_rows(np.random.default_rng(B * 31 + K + V), B, K, V, tau)
+    tl, dl, dt, ud = _dev(lp, lq, t, u)
+    out = []
+    for f in (sv.sv_verify_sample_logits_early_batched, sv.sv_verify_sample_logits_batched):
+        ws = torch.empty(sv.sv_workspace_size(B, K, V, True), dtype=torch.uint8, device=DEV)
+        sv.sv_workspace_init(ws)
+        n, nx = f(tl, dl, dt, ud, tau, workspace=ws)
+        torch.cuda.synchronize()
+        out += [n.cpu().numpy(), nx.cpu().numpy()]
+    assert np.array_equal(out[0], out[2]) and np.array_equal(out[1], out[3])
+    check(out[0], out[1], verify_sample_logits(lp, lq, t, u, tau))
+
+
+def test_early_logits_full_workload():
+    """B=256 K=5 V=128256 logits (the synthetic mix), tau = 1, four calls on
+    one workspace over two input sets: every output equal to the full
+    logits pass's."""
+    c = dict(workloads.CONFIGS[3])
+    B, K, V = c["B"], c["K"], c["V"]
+    _case(f"early exit logits full workload B={B} K={K} V={V} (generating)")
+    sets = [device_batch(c["family"], B, K, V, seed=s, device=DEV, sampled=True, logits=True) for s in range(2)]
+    ws = torch.empty(sv.sv_workspace_size(B, K, V, True), dtype=torch.uint8, device=DEV)
+    sv.sv_workspace_init(ws)
+    for rep in range(4):
+        db = sets[rep % 2]
+        n, nx = sv.sv_verify_sample_logits_batched(db["tp"], db["dp"], db["dt"], db["u"], 1.0, workspace=ws)
+        en, ex = sv.sv_verify_sample_logits_early_batched(db["tp"], db["dp"], db["dt"], db["u"], 1.0, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(en, n) and torch.equal(ex, nx), rep
+    assert 0 < int((n < K).sum()) < B
+    del sets
+    torch.cuda.empty_cache()
