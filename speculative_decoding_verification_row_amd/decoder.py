@@ -51,7 +51,7 @@ from typing import Callable, List, Optional, Sequence
 import numpy as np
 import torch
 
-from . import sv_verify_greedy_batched, sv_verify_sample_batched, workspace_for
+from . import sv_verify_greedy_batched, sv_verify_sample_early_batched, workspace_for
 
 
 @dataclass
@@ -208,8 +208,10 @@ class SpeculativeDecoder:
                   _as_f32(dprobs, dev, (b, k, V)))
             bufs["u_host"][...] = u
             bufs["u_dev"].copy_(bufs["u_pin"], non_blocking=True)
-            sv_verify_sample_batched(tp, dp, tk, bufs["u_dev"], n_accepted=bufs["n"], next_token=bufs["x"],
-                                     workspace=ws, stream=stream)
+            # the early exit: the full pass's outputs, bit for bit, reading
+            # only the rows they depend on (the driver takes no statistics)
+            sv_verify_sample_early_batched(tp, dp, tk, bufs["u_dev"], n_accepted=bufs["n"], next_token=bufs["x"],
+                                           workspace=ws, stream=stream)
         if host_toks is None:
             dev_out[:o].copy_(tk.reshape(-1))
         if forcing:
