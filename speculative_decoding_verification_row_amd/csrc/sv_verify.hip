@@ -135,6 +135,7 @@ struct Args {
     float ktau;                      // logits: log2(e) / temperature
     double ktau64;                   // the same in fp64 (acceptance weights)
     int early;                       // sampled: read no row a decided sequence no longer needs
+    int force_lost;                  // test hook: every in-walk decision gives up (readers still trust partials)
 };
 
 // ------------------------------------------- cross-block communication --
@@ -1025,7 +1026,7 @@ __device__ int poll_decide(const Args& a, int b, int i, Poll pl, double* P, doub
                 w1q = get_u64(&p1->sq);
             }
         }
-        if (__ballot(need0 || need1) == 0ull) {
+        if (__ballot(need0 || need1) == 0ull && !a.force_lost) {
             const double p = wave_sum(s0p + s1p), q = wave_sum(s0q + s1q);
             if (t == 0) {
                 s_PQ[0] = p;
@@ -1380,8 +1381,9 @@ __global__ __launch_bounds__(kThreads, 4) void sv_sample_kernel(Args a)
         publish_part<MP>(a, row0 + i, c, block_reduce<MP, false>(thread_stats<MP, kVecS>(xp, xq, c), i & 1));
         if (pending) decide(i - 1, pl);
         // the early exit issues row i+1's loads only once row i-1 is
-        // accepted, so that a rejection at n leaves rows n+2.. unread
-        if (EARLY && state == kSearching) load_next(i);
+        // accepted (or its decision is lost: the walk then still streams
+        // every row), so that a rejection at n leaves rows n+2.. unread
+        if (EARLY && state < 0) load_next(i);
         if (state == kSearching) park(xp, xq);
 #pragma unroll
         for (int k = 0; k < kVecS; ++k) {
@@ -1765,7 +1767,7 @@ __device__ int poll_decide_l(const Args& a, int b, int i, PollL pl, LRow* out)
                 w1[3] = get_u64(&p1->smin);
             }
         }
-        if (__ballot(need0 || need1) == 0ull) {
+        if (__ballot(need0 || need1) == 0ull && !a.force_lost) {
             LRow r;
             r.P = row_mass_l(m0p, s0p, m1p, s1p, k, &r.Mp);
             r.Q = row_mass_l(m0q, s0q, m1q, s1q, k, &r.Mq);
@@ -2303,7 +2305,7 @@ __global__ __launch_bounds__(kThreads, 4) void sv_logits_kernel(Args a)
         __builtin_amdgcn_sched_barrier(0);
         publish_l(a, row0 + i, c, chunk_stats_l<kVecS, true>(xp, xq, c, V, kt, i & 1), true);
         if (pending) decide(i - 1, pl);
-        if (EARLY && state == kSearching) load_next(i);   // early exit: loads after the decision
+        if (EARLY && state < 0) load_next(i);   // early exit: loads after the decision (searching or lost)
         if (state == kSearching) park(xp, xq);
 #pragma unroll
         for (int j = 0; j < kVecS; ++j) {
@@ -2370,17 +2372,22 @@ struct Tuning {
     double poll_us = kPollMicroseconds;
     int force_recompute = 0;
     int rows = -1;           // sampled form: -1 by size, 0 walks, 1 one block per row
+    int force_lost = 0;
 };
 
 // Read at every call: SV_VERIFY_POLL_US bounds a wait for a sibling's
 // partials; SV_VERIFY_FORCE_RECOMPUTE=1 makes every reader recompute what it
-// gathers (a test hook for the recompute path).
+// gathers (a test hook for the recompute path); SV_VERIFY_FORCE_LOST=1 makes
+// every decision taken inside a walk or row block report that its partials
+// did not arrive, while the readers that finish a sequence still trust the
+// published words (a test hook for the lost-decision path).
 Tuning tuning()
 {
     Tuning r;
     if (const char* s = std::getenv("SV_VERIFY_POLL_US")) r.poll_us = std::atof(s);
     if (const char* s = std::getenv("SV_VERIFY_FORCE_RECOMPUTE")) r.force_recompute = std::atoi(s) != 0;
     if (const char* s = std::getenv("SV_VERIFY_ROWS")) r.rows = std::atoi(s) != 0 ? 1 : 0;
+    if (const char* s = std::getenv("SV_VERIFY_FORCE_LOST")) r.force_lost = std::atoi(s) != 0;
     if (!(r.poll_us >= 0.0) || r.poll_us > 1e7) r.poll_us = kPollMicroseconds;
     return r;
 }
@@ -2598,6 +2605,7 @@ sv_status sv_verify_greedy_batched(const float* target_probs, const int32_t* dra
     a.stats = stats;
     const Tuning tu = tuning();
     a.force_recompute = tu.force_recompute;
+    a.force_lost = tu.force_lost;
     a.poll_ticks = (unsigned long long)(tu.poll_us * 1e-3 * (double)d.wall_khz);
     const bool vec = (V % 4 == 0) && aligned(target_probs, 16);
     const dim3 grid((unsigned)((uint64_t)B * (uint64_t)(K + 1) * (uint64_t)a.NC));
@@ -2671,6 +2679,7 @@ sv_status sample_call(const float* target_probs, const float* draft_probs,
     a.early = early ? 1 : 0;
     const Tuning tu = tuning();
     a.force_recompute = tu.force_recompute;
+    a.force_lost = tu.force_lost;
     a.poll_ticks = (unsigned long long)(tu.poll_us * 1e-3 * (double)d.wall_khz);
     const bool vec = (V % 4 == 0) && aligned(target_probs, 16) && (K == 0 || aligned(draft_probs, 16));
     const uint64_t per_row = (uint64_t)B * (uint64_t)a.NC;
@@ -2750,6 +2759,7 @@ sv_status logits_call(const float* target_logits, const float* draft_logits,
     a.ktau = (float)a.ktau64;
     const Tuning tu = tuning();
     a.force_recompute = tu.force_recompute;
+    a.force_lost = tu.force_lost;
     a.poll_ticks = (unsigned long long)(tu.poll_us * 1e-3 * (double)d.wall_khz);
     const bool vec = (V % 4 == 0) && aligned(target_logits, 16) && (K == 0 || aligned(draft_logits, 16));
     const uint64_t per_row = (uint64_t)B * (uint64_t)a.NC;
