@@ -117,6 +117,9 @@ def verify_sample(target_probs, draft_probs, draft_tokens, uniforms, threads: in
     rc = _load().svo_verify_sample(_ptr(tp), _ptr(dp), _ptr(dt), _ptr(u), B, K, V,
                                    _ptr(n), _ptr(nxt), _ptr(st), _ptr(dg), _ptr(al),
                                    int(threads))
+    if rc == -4:
+        raise OracleError("oracle sampled: the inverse CDF found no token, which the proof in "
+                          "sv_oracle.c rules out for valid inputs")
     if rc != 0:
         raise OracleError(f"oracle sampled: precondition violated (rc={rc})")
     out = {"n_accepted": n, "next_token": nxt}

@@ -19,6 +19,13 @@ of the probability oracle (sv_oracle.c) on these fp64 weights:
   next = the smallest x whose running sum exceeds u_K * (total), else (by
   rounding only) the last x with positive weight.
 A draft token outside [0, V) has zero weight on both sides and is rejected.
+
+The last rule (the rounding guard) is reachable only when the searched
+total W is below fp64's normal range: for a normal W, u_K * W rounds below W
+(u_K <= 1 - 2^-24), and the running sum reaches W at the last position.  A
+residual can be that small only when every position where the target
+outweighs the draft has a weight below about 2^-1000, e.g. a target logit
+745 * tau under its row's maximum against a draft weight of 0.
 """
 from __future__ import annotations
 

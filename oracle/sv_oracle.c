@@ -41,8 +41,19 @@
  *       with u_0.
  *   R10 inputs must be finite and non-negative, each P and Q positive, each
  *       uniform in [0, 1); otherwise the call fails (returns -1).
- *   Guard: if rounding leaves no x with C(x) > T, the last x with w(x) > 0
- *       is returned (flagged in the diagnostics).
+ *
+ * The inverse CDF always finds its token (no rounding guard is needed).  The
+ * running mass at the last token, C(V-1), is the same sequential fp64 sum as
+ * the total W (same terms, same order), so C(V-1) == W bitwise.  W is a
+ * normal fp64 number: for a draw from a row it is that row's mass, at least
+ * 2^-149 (the smallest positive f32); for a residual, every term p*Q and q*P
+ * is a product of an f32 (a multiple of 2^-149) and an fp64 mass of at least
+ * 2^-149, so each rounded product is a multiple of 2^-350, and a positive
+ * difference of two of them rounds to at least 2^-350.  With u <= 1 - 2^-24
+ * (the largest f32 below 1) the product u*W is 0 or normal, and rounding to
+ * nearest gives T = fl(u*W) <= (1 - 2^-24)(1 + 2^-53) W < W = C(V-1).  So
+ * some x has C(x) > T.  The oracle checks this and returns -4 if it ever
+ * failed, rather than picking a token by another rule.
  *
  * Build: gcc -O2 -std=c11 -fPIC -shared -ffp-contract=off -pthread
  * (never -ffast-math).  oracle/build.py runs exactly that.
@@ -68,8 +79,7 @@ typedef struct {
     int32_t n_accepted;
     int32_t next_token;
     int32_t draw_row;      /* row whose distribution the final draw searched */
-    int32_t draw_kind;     /* 1 residual, 2 bonus, 3 residual fell back to p_n;
-                              +4 when the rounding guard picked the token */
+    int32_t draw_kind;     /* 1 residual, 2 bonus, 3 residual fell back to p_n (R8) */
     double accept_margin;  /* min over performed tests of |u q(t) P - p(t) Q| / (q(t) P);
                               +inf when no test was performed or q(t) P == 0 */
     double draw_margin;    /* min(T - C(x-1), C(x) - T) / W at the selected x */
@@ -224,23 +234,16 @@ static int sample_one(const float* p, const float* q, const int32_t* t, const fl
     }
     double T = (double)u[K] * W;
     double C = 0.0, Cprev = 0.0;
-    int64_t pick = -1, last_pos = -1;
+    int64_t pick = -1;
     for (int64_t x = 0; x < V; ++x) {
         double w = qw ? residual_w(pw, qw, P[n], Q[n], x) : (double)pw[x];
-        if (w > 0.0) last_pos = x;
         Cprev = C;
         C += w;
         if (C > T) { pick = x; break; }
     }
-    double dmargin;
-    if (pick < 0) {              /* rounding guard */
-        pick = last_pos;
-        kind += 4;
-        dmargin = 0.0;
-    } else {
-        double lo = T - Cprev, hi = C - T;
-        dmargin = (lo < hi ? lo : hi) / W;
-    }
+    if (pick < 0) return -4;     /* unreachable (see the note at the top) */
+    double lo = T - Cprev, hi = C - T;
+    double dmargin = (lo < hi ? lo : hi) / W;
     *n_out = n;
     *next_out = (int32_t)pick;
     if (dg) {
@@ -336,7 +339,9 @@ int svo_verify_greedy(const float* tp, const int32_t* dt, int64_t B, int32_t K, 
 /* Sampled verification of B sequences.  tp [B, K+1, V], dp [B, K, V] f32,
  * dt [B, K] int32, u [B, K+1] f32.  Writes n_accepted, next_token and, if
  * non-NULL, stats [B, K+1], diag [B] and alpha [B, K] (the normalised
- * per-row acceptance sum_x min(p/P, q/Q)). */
+ * per-row acceptance sum_x min(p/P, q/Q)).  Returns 0, -1 on a violated
+ * precondition, -2 on bad sizes, -4 if the inverse CDF found no token
+ * (impossible for valid inputs; see the note at the top). */
 int svo_verify_sample(const float* tp, const float* dp, const int32_t* dt, const float* u,
                       int64_t B, int32_t K, int64_t V,
                       int32_t* n_accepted, int32_t* next_token, svo_row_stats* stats,

@@ -21,9 +21,10 @@ import workloads
 from workloads.device import device_batch
 import speculative_decoding_verification_row_amd as sv
 
+from _parity import BAND_LOGITS, boundary_mask, check_logits
+
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
-BAND = 1e-5
 
 
 def _case(msg):
@@ -48,17 +49,10 @@ def form(request, monkeypatch):
 
 
 def _boundary(d):
-    return (d["accept_margin"] <= BAND) | (d["draw_margin"] <= BAND) | (d["draw_kind"] >= 4)
+    return boundary_mask(d, BAND_LOGITS)
 
 
-def check(n, nx, o):
-    bnd = _boundary(o["diag"])
-    same = (n == o["n_accepted"]) & (nx == o["next_token"])
-    bad = ~same & ~bnd
-    assert not bad.any(), (f"{int(bad.sum())} non-boundary mismatches; first at {int(np.flatnonzero(bad)[0])}: "
-                           f"gpu ({int(n[bad][0])}, {int(nx[bad][0])}) oracle "
-                           f"({int(o['n_accepted'][bad][0])}, {int(o['next_token'][bad][0])})")
-    return {"sequences": int(n.size), "boundary": int(bnd.sum()), "boundary_mismatch": int((~same & bnd).sum())}
+check = check_logits
 
 
 def run(tl, dl, t, u, tau, offset=False, **kw):

@@ -26,6 +26,7 @@ import oracle
 from oracle.logits import verify_sample_logits, warp_row
 
 from test_oracle_law import _cells
+from _parity import boundary_mask
 
 
 def _logit_instance(rng, K, V, zeros=True):
@@ -67,7 +68,7 @@ def test_logits_enumeration_preserves_warped_law(K, V, tau, seed):
 
 
 def _boundary(d):
-    return (d["accept_margin"] <= 1e-5) | (d["draw_margin"] <= 1e-5) | (d["draw_kind"] >= 4)
+    return boundary_mask(d, 1e-5)
 
 
 @pytest.mark.parametrize("tau", [0.6, 1.0, 1.7])
@@ -170,3 +171,62 @@ def test_low_temperature_limit_is_greedy_verification():
     assert np.array_equal(r["next_token"], g["next_token"])
     # every outcome occurs
     assert set(np.unique(g["n_accepted"])) == set(range(K + 1))
+
+
+def test_logits_zero_residual_draws_from_target_row():
+    """R8 on logits: draft logits equal to the target's bit for bit give
+    identical weights and masses, so a rejected token (out of range here)
+    leaves a residual of exactly 0 and the draw is inverse-CDF sampling of
+    the warped target row n with u_K; the expected token comes from scipy's
+    softmax of l / tau (outside a 1e-9 band around the CDF's breakpoints)."""
+    rng = np.random.default_rng(808)
+    B, K, V, tau = 40, 4, 700, 0.8
+    lp = rng.normal(0, 2.0, (B, K + 1, V)).astype(np.float32)
+    lq = (lp[:, :K] + rng.normal(0, 1.0, (B, K, V))).astype(np.float32)
+    t = rng.integers(0, V, size=(B, K)).astype(np.int32)
+    u = rng.random((B, K + 1), dtype=np.float32)
+    nsel = rng.integers(0, K, size=B)
+    for b in range(B):
+        n = int(nsel[b])
+        lq[b, :n + 1] = lp[b, :n + 1]                 # rows 0..n: identical warps
+        t[b, :n] = np.argmax(lp[b, :n], axis=1)       # accepted with certainty
+        t[b, n] = V if b % 2 else -1                  # rejected
+    r = verify_sample_logits(lp, lq, t, u, tau)
+    tau32 = float(np.float32(tau))
+    checked = 0
+    for b in range(B):
+        n = int(nsel[b])
+        assert int(r["n_accepted"][b]) == n
+        assert int(r["diag"]["draw_kind"][b]) == 3
+        c = np.cumsum(softmax(lp[b, n].astype(np.float64) / tau32))
+        T = float(u[b, K]) * c[-1]
+        if np.min(np.abs(c - T)) <= 1e-9 * c[-1]:
+            continue
+        assert int(r["next_token"][b]) == int(np.searchsorted(c, T, side="right"))
+        checked += 1
+    assert checked >= B - 2
+
+
+def test_logits_rounding_guard_hand_derived():
+    """The guard's one reachable case, derived by hand.  V = 2, K = 1,
+    tau = 1.  Target row 0 has logits (0, -744.4): weights 1 and
+    exp(-744.4), which rounds to the smallest fp64 subnormal 2^-1074; its
+    mass 1 + 2^-1074 rounds to 1.  Draft row 0 has logits (0, -2000):
+    weights 1 and 0, mass 1.  The token 2 is outside [0, 2), so it is
+    rejected, and the residual max(0, w_p Q - w_q P) is (0, 2^-1074):
+    W = 2^-1074.  With u_1 = 0.75, T = 0.75 * 2^-1074 rounds to 2^-1074 = W,
+    no running sum exceeds T, and the guard takes the last position with
+    weight, 1 (draw kind 1 + 4).  With u_1 = 0.25, T rounds to 0 and the
+    running sum 2^-1074 at position 1 exceeds it: the ordinary rule gives
+    position 1 (kind 1) with a draw margin of 0 (T equals C(0) = 0)."""
+    lp = np.array([[[0.0, -744.4], [0.0, 0.0]]], np.float32)
+    lq = np.array([[[0.0, -2000.0]]], np.float32)
+    t = np.array([[2]], np.int32)
+    r = verify_sample_logits(lp, lq, t, np.array([[0.5, 0.75]], np.float32), 1.0)
+    d = r["diag"][0]
+    assert (int(r["n_accepted"][0]), int(r["next_token"][0])) == (0, 1)
+    assert int(d["draw_kind"]) == 5 and d["W"] == 2.0 ** -1074 and d["T"] == 2.0 ** -1074
+    r = verify_sample_logits(lp, lq, t, np.array([[0.5, 0.25]], np.float32), 1.0)
+    d = r["diag"][0]
+    assert (int(r["next_token"][0]), int(d["draw_kind"])) == (1, 1)
+    assert d["T"] == 0.0 and d["draw_margin"] == 0.0

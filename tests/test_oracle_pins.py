@@ -37,6 +37,21 @@ def test_golden_hand_derived(oracle_mod, case):
         r = oracle_mod.verify_sample(p, q, t, u)
     assert int(r["n_accepted"][0]) == case["expect"]["n_accepted"]
     assert int(r["next_token"][0]) == case["expect"]["next_token"]
+    if "draw_kind" in case["expect"]:
+        d = r["diag"][0]
+        assert int(d["draw_kind"]) == case["expect"]["draw_kind"]
+        for f in ("accept_margin", "draw_margin"):
+            want = _fraction(case["expect"][f])
+            got = float(d[f])
+            assert (got == want) if math.isinf(want) else abs(got - want) <= 1e-15 * max(1.0, want), (f, got, want)
+
+
+def _fraction(s: str) -> float:
+    """'inf', '0', '1/6' -> float."""
+    if s == "inf":
+        return math.inf
+    num, _, den = s.partition("/")
+    return float(num) / float(den or 1)
 
 
 # ------------------------------------------------------------ greedy (P-a) --
