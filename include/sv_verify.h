@@ -62,12 +62,17 @@ typedef enum {
     SV_ERR_INVALID_ARG = -1,  /* NULL pointer, negative size, misaligned pointer */
     SV_ERR_WORKSPACE = -2,    /* workspace NULL, misaligned or smaller than sv_workspace_size */
     SV_ERR_HIP = -3,          /* a HIP runtime call or kernel launch failed */
-    SV_ERR_UNSUPPORTED = -4   /* sizes beyond the supported maximum (V > SV_MAX_V, K > SV_MAX_K) */
+    SV_ERR_UNSUPPORTED = -4,  /* sizes beyond the supported maximum (V > SV_MAX_V, K > SV_MAX_K) */
+    SV_ERR_SCRATCH = -5       /* the call needs more workspace than SV_SCRATCH_BYTES (no-allocation entry point) */
 } sv_status;
 
 /* Largest vocabulary and draft length the kernels accept. */
 #define SV_MAX_V 524288
 #define SV_MAX_K 4096
+
+/* Bytes of the library's static device scratch, one copy per device (the
+ * workspace of sv_verify_sample_batched_noalloc). */
+#define SV_SCRATCH_BYTES (16u << 20)
 
 /* Per-row statistics, one per (b, i), i in [0, K], 48 bytes.
  *   argmax, max_p : lowest index of the maximum of p_i, and that value
@@ -182,6 +187,30 @@ sv_status sv_verify_sample_logits_early_batched(const float* target_logits, cons
                                                 float temperature, int32_t B, int32_t K, int32_t V,
                                                 int32_t* n_accepted, int32_t* next_token,
                                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the call of
+ * sv_verify_sample_batched, same arguments and outputs, without a workspace.
+ * Its workspace is a static device array of SV_SCRATCH_BYTES that the
+ * library's code object holds on every device it runs on until the process
+ * ends; the library looks up that array's address on a device at the first
+ * call there (hipGetSymbolAddress) and calls no hipMalloc, hipFree or other
+ * allocating routine.  Every call on one device shares that device's array
+ * and finds the words the previous call left there; they carry that call's
+ * tag and are ignored (the first call on a device, and every 255th after it,
+ * clears the part it uses with a fill kernel on its stream).  Calls that
+ * overlap on one device race on the array: issue them in order on one
+ * stream, or wait between streams.  Like every call with a workspace, it
+ * must not be captured into a HIP graph that is replayed.
+ * Errors: those of sv_verify_sample_batched (SV_ERR_WORKSPACE excepted), and
+ * SV_ERR_SCRATCH when sv_workspace_size(B, K, V, 1) > SV_SCRATCH_BYTES
+ * (11.5 MB at B = 1024, K = 8, V = 128256 fits), returned before anything is
+ * launched. */
+sv_status sv_verify_sample_batched_noalloc(const float* target_probs, const float* draft_probs,
+                                           const int32_t* draft_tokens, const float* uniforms,
+                                           int32_t B, int32_t K, int32_t V,
+                                           int32_t* n_accepted, int32_t* next_token,
+                                           sv_row_stats* stats, void* stream);
 
 /* Synchronously read the workspace's device-fault word into *error_out
  * (host memory), waiting for `stream` first: 0 when every call since the

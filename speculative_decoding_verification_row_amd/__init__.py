@@ -35,6 +35,7 @@ __all__ = [
     "sv_workspace_size", "sv_workspace_init", "sv_workspace_error", "sv_status_string",
     "sv_verify_greedy_batched", "sv_verify_sample_batched", "sv_verify_sample_early_batched",
     "sv_verify_sample_logits_batched", "sv_verify_sample_logits_early_batched",
+    "sv_verify_sample_batched_noalloc", "SV_SCRATCH_BYTES",
     "verify_greedy", "verify_sample", "stats_to_numpy", "workspace_for",
     "SpeculativeDecoder", "DecodeStats", "Governor",
 ]
@@ -42,7 +43,8 @@ __all__ = [
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libsv_verify.so")
 
-SV_OK, SV_ERR_INVALID_ARG, SV_ERR_WORKSPACE, SV_ERR_HIP, SV_ERR_UNSUPPORTED = 0, -1, -2, -3, -4
+SV_OK, SV_ERR_INVALID_ARG, SV_ERR_WORKSPACE, SV_ERR_HIP, SV_ERR_UNSUPPORTED, SV_ERR_SCRATCH = 0, -1, -2, -3, -4, -5
+SV_SCRATCH_BYTES = 16 << 20   # the library's static device scratch (include/sv_verify.h)
 
 # layout of sv_row_stats (48 bytes)
 ROW_STATS_DTYPE = np.dtype([
@@ -92,6 +94,8 @@ def load_library():
     lib.sv_verify_sample_logits_batched.restype = ctypes.c_int
     lib.sv_verify_sample_logits_early_batched.argtypes = [P, P, P, P, ctypes.c_float, I32, I32, I32, P, P, P, SZ, P]
     lib.sv_verify_sample_logits_early_batched.restype = ctypes.c_int
+    lib.sv_verify_sample_batched_noalloc.argtypes = [P, P, P, P, I32, I32, I32, P, P, P, P]
+    lib.sv_verify_sample_batched_noalloc.restype = ctypes.c_int
     lib.sv_workspace_error.argtypes = [P, ctypes.POINTER(I32), P]
     lib.sv_workspace_error.restype = ctypes.c_int
     lib.sv_status_string.argtypes = [ctypes.c_int]
@@ -367,6 +371,35 @@ def sv_verify_sample_logits_early_batched(target_logits: torch.Tensor, draft_log
     if rc != SV_OK:
         raise SVError(rc, "sv_verify_sample_logits_early_batched")
     return n_accepted, next_token
+
+def sv_verify_sample_batched_noalloc(target_probs: torch.Tensor, draft_probs: torch.Tensor,
+                                     draft_tokens: torch.Tensor, uniforms: torch.Tensor,
+                                     n_accepted: torch.Tensor, next_token: torch.Tensor,
+                                     stats=None, stream=None):
+    """sv_verify_sample_batched without a workspace: the library's static
+    device scratch serves instead (SV_SCRATCH_BYTES per device).  For callers
+    that cannot allocate, the outputs (and a [B, K+1, 48] uint8 stats tensor,
+    if wanted) must be preallocated: this binding allocates nothing either.
+    Calls that overlap on one device race on the scratch."""
+    B, K1, V = target_probs.shape
+    K = K1 - 1
+    dev = _device_of(target_probs, "target_probs")
+    _check(target_probs, "target_probs", torch.float32, (B, K1, V), dev)
+    _check(draft_probs, "draft_probs", torch.float32, (B, K, V), dev)
+    _check(draft_tokens, "draft_tokens", torch.int32, (B, K), dev)
+    _check(uniforms, "uniforms", torch.float32, (B, K1), dev)
+    _check(n_accepted, "n_accepted", torch.int32, (B,), dev)
+    _check(next_token, "next_token", torch.int32, (B,), dev)
+    if stats is not None:
+        _check(stats, "stats", torch.uint8, (B, K1, 48), dev)
+    rc = _call(dev, load_library().sv_verify_sample_batched_noalloc,
+               target_probs.data_ptr(), draft_probs.data_ptr(), draft_tokens.data_ptr(), uniforms.data_ptr(),
+               B, K, V, n_accepted.data_ptr(), next_token.data_ptr(),
+               None if stats is None else stats.data_ptr(), _stream_handle(stream, dev))
+    if rc != SV_OK:
+        raise SVError(rc, "sv_verify_sample_batched_noalloc")
+    return n_accepted, next_token
+
 
 def stats_to_numpy(stats: torch.Tensor) -> np.ndarray:
     """[B, K+1, 48] uint8 device tensor -> [B, K+1] ROW_STATS_DTYPE array."""

@@ -64,6 +64,11 @@
 
 #pragma clang fp contract(off)
 
+// The workspace of sv_verify_sample_batched_noalloc, one copy per device.
+// In host code this name is only a handle for hipGetSymbolAddress; the
+// device address it resolves to is what the kernels receive.
+static __device__ __align__(256) unsigned char scratch[SV_SCRATCH_BYTES];
+
 namespace {
 
 constexpr int kThreads = 256;
@@ -2491,19 +2496,24 @@ sv_status launch_fill(void* ws, size_t bytes, hipStream_t s)
 // with more bytes than any earlier call at that address (the new part was
 // never cleared), and every call after kEpochs tags have been used clear the
 // whole extent of the workspace seen so far on `s` first, so no word left by
-// an earlier call can carry a tag in use.
-sv_status next_epoch(void* ws, size_t bytes, hipStream_t s, unsigned* ep)
+// an earlier call can carry a tag in use.  `fixed` (the static scratch)
+// holds its own state, so that call takes no map entry.
+sv_status next_epoch(void* ws, size_t bytes, hipStream_t s, unsigned* ep, WsState* fixed = nullptr)
 {
     bool clear = false;
     size_t extent = 0;
     {
         std::lock_guard<std::mutex> lk(g_mu);
-        auto it = g_ws.find(ws);
-        if (it == g_ws.end()) {
-            it = g_ws.emplace(ws, WsState{}).first;
-            it->second.calls = kEpochs;   // unknown contents: clear first
+        WsState* stp = fixed;
+        if (!stp) {
+            auto it = g_ws.find(ws);
+            if (it == g_ws.end()) {
+                it = g_ws.emplace(ws, WsState{}).first;
+                it->second.calls = kEpochs;   // unknown contents: clear first
+            }
+            stp = &it->second;
         }
-        WsState& st = it->second;
+        WsState& st = *stp;
         if (bytes > st.bytes) {   // the part beyond the extent cleared so far holds unknown words
             st.bytes = bytes;
             st.calls = kEpochs;
@@ -2516,6 +2526,37 @@ sv_status next_epoch(void* ws, size_t bytes, hipStream_t s, unsigned* ep)
         extent = st.bytes;
     }
     return clear ? launch_fill(ws, extent, s) : SV_OK;
+}
+
+// Per device: the device address of `scratch` and the tag state of that
+// array, filled by the first no-allocation call on the device.
+struct ScratchDev {
+    void* ptr = nullptr;
+    WsState st;
+};
+ScratchDev g_scratch[64];
+
+// The current device's copy of `scratch` (looked up once per device, with
+// that device current) and its tag state.
+sv_status scratch_of_device(void** ptr, WsState** state)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return SV_ERR_HIP;
+    std::lock_guard<std::mutex> lk(g_mu);
+    ScratchDev& d = g_scratch[dev];
+    if (!d.ptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return SV_ERR_HIP;
+        }
+        d.ptr = p;
+        d.st.calls = kEpochs;   // contents unknown: the first call clears what it uses
+        d.st.bytes = 0;
+    }
+    *ptr = d.ptr;
+    *state = &d.st;
+    return SV_OK;
 }
 
 Args make_args(void* ws, int32_t B, int32_t K, int32_t V, bool sampled)
@@ -2538,13 +2579,17 @@ Args make_args(void* ws, int32_t B, int32_t K, int32_t V, bool sampled)
 }  // namespace
 
 namespace {
+sv_status check_sample_args(const float* target_probs, const float* draft_probs,
+                            const int32_t* draft_tokens, const float* uniforms,
+                            int32_t B, int32_t K, int32_t V,
+                            const int32_t* n_accepted, const int32_t* next_token, const sv_row_stats* stats);
 // The body of both sampled entry points (early: the early-exit form).
 sv_status sample_call(const float* target_probs, const float* draft_probs,
                       const int32_t* draft_tokens, const float* uniforms,
                       int32_t B, int32_t K, int32_t V,
                       int32_t* n_accepted, int32_t* next_token,
                       void* workspace, size_t workspace_bytes,
-                      sv_row_stats* stats, void* stream, bool early);
+                      sv_row_stats* stats, void* stream, bool early, WsState* fixed = nullptr);
 // The body of both logits entry points.
 sv_status logits_call(const float* target_logits, const float* draft_logits,
                       const int32_t* draft_tokens, const float* uniforms, float temperature,
@@ -2640,17 +2685,36 @@ sv_status sv_verify_sample_early_batched(const float* target_probs, const float*
     return sample_call(target_probs, draft_probs, draft_tokens, uniforms, B, K, V, n_accepted, next_token,
                        workspace, workspace_bytes, nullptr, stream, true);
 }
+
+sv_status sv_verify_sample_batched_noalloc(const float* target_probs, const float* draft_probs,
+                                           const int32_t* draft_tokens, const float* uniforms,
+                                           int32_t B, int32_t K, int32_t V,
+                                           int32_t* n_accepted, int32_t* next_token,
+                                           sv_row_stats* stats, void* stream)
+{
+    const sv_status st = check_sample_args(target_probs, draft_probs, draft_tokens, uniforms, B, K, V,
+                                           n_accepted, next_token, stats);
+    if (st != SV_OK || B == 0) return st;
+    const size_t need = sv_workspace_size(B, K, V, 1);
+    if (need > (size_t)SV_SCRATCH_BYTES) return SV_ERR_SCRATCH;
+    void* ws = nullptr;
+    WsState* state = nullptr;
+    const sv_status ss = scratch_of_device(&ws, &state);
+    if (ss != SV_OK) return ss;
+    return sample_call(target_probs, draft_probs, draft_tokens, uniforms, B, K, V, n_accepted, next_token,
+                       ws, need, stats, stream, false, state);
+}
 }   // extern "C"
 
 namespace {
-sv_status sample_call(const float* target_probs, const float* draft_probs,
-                      const int32_t* draft_tokens, const float* uniforms,
-                      int32_t B, int32_t K, int32_t V,
-                      int32_t* n_accepted, int32_t* next_token,
-                      void* workspace, size_t workspace_bytes,
-                      sv_row_stats* stats, void* stream, bool early)
+// The argument checks of the sampled calls (sizes, NULL and misaligned
+// pointers), before anything else is done.
+sv_status check_sample_args(const float* target_probs, const float* draft_probs,
+                            const int32_t* draft_tokens, const float* uniforms,
+                            int32_t B, int32_t K, int32_t V,
+                            const int32_t* n_accepted, const int32_t* next_token, const sv_row_stats* stats)
 {
-    sv_status st = check_sizes(B, K, V);
+    const sv_status st = check_sizes(B, K, V);
     if (st != SV_OK) return st;
     if (B == 0) return SV_OK;   // nothing to verify; pointers are not inspected
     if (!target_probs || !uniforms || !n_accepted || !next_token ||
@@ -2660,6 +2724,19 @@ sv_status sample_call(const float* target_probs, const float* draft_probs,
         !aligned(uniforms, 4) || !aligned(n_accepted, 4) || !aligned(next_token, 4) ||
         !aligned(stats, 8))
         return SV_ERR_INVALID_ARG;
+    return SV_OK;
+}
+
+sv_status sample_call(const float* target_probs, const float* draft_probs,
+                      const int32_t* draft_tokens, const float* uniforms,
+                      int32_t B, int32_t K, int32_t V,
+                      int32_t* n_accepted, int32_t* next_token,
+                      void* workspace, size_t workspace_bytes,
+                      sv_row_stats* stats, void* stream, bool early, WsState* fixed)
+{
+    sv_status st = check_sample_args(target_probs, draft_probs, draft_tokens, uniforms, B, K, V, n_accepted,
+                                      next_token, stats);
+    if (st != SV_OK || B == 0) return st;
     if (!workspace || !aligned(workspace, 16) || workspace_bytes < sv_workspace_size(B, K, V, 1))
         return SV_ERR_WORKSPACE;
     DevInfo d;
@@ -2667,7 +2744,7 @@ sv_status sample_call(const float* target_probs, const float* draft_probs,
     if (st != SV_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     Args a = make_args(workspace, B, K, V, true);
-    st = next_epoch(workspace, workspace_bytes, s, &a.epoch);
+    st = next_epoch(workspace, workspace_bytes, s, &a.epoch, fixed);
     if (st != SV_OK) return st;
     a.tp = target_probs;
     a.dp = draft_probs;
@@ -2806,6 +2883,7 @@ const char* sv_status_string(sv_status s)
     case SV_ERR_WORKSPACE: return "SV_ERR_WORKSPACE: workspace missing, misaligned or too small";
     case SV_ERR_HIP: return "SV_ERR_HIP: a HIP runtime call or kernel launch failed";
     case SV_ERR_UNSUPPORTED: return "SV_ERR_UNSUPPORTED: size beyond the supported maximum";
+    case SV_ERR_SCRATCH: return "SV_ERR_SCRATCH: the call needs more than the static scratch (SV_SCRATCH_BYTES)";
     }
     return "unknown sv_status";
 }

@@ -54,7 +54,7 @@ def test_library_is_built_for_gfx950(lib):
 def test_status_strings(lib):
     import speculative_decoding_verification_row_amd as sv
     assert sv.sv_status_string(0) == "SV_OK"
-    for code in (-1, -2, -3, -4):
+    for code in (-1, -2, -3, -4, -5):
         assert sv.sv_status_string(code).startswith("SV_ERR_")
     assert "unknown" in sv.sv_status_string(7)
 
@@ -175,3 +175,31 @@ def test_kernel_argument_pointer_is_taken_in_kernel_bodies_only():
             continue                                            # a comment
         head = _enclosing_function(text, pos)
         assert head.startswith("__global__"), f"line {line}: inside `{head}`"
+
+
+def test_argument_errors_sampled_noalloc(lib):
+    """The no-allocation entry point: the sampled call's argument checks, and
+    SV_ERR_SCRATCH (-5) for sizes whose workspace exceeds SV_SCRATCH_BYTES,
+    all before anything is launched."""
+    import speculative_decoding_verification_row_amd as sv
+
+    def na(tp=FAKE, dp=FAKE, dt=FAKE, u=FAKE, B=1, K=1, V=8, n=FAKE, st=None):
+        return lib.sv_verify_sample_batched_noalloc(tp, dp, dt, u, B, K, V, n, FAKE, st, None)
+    assert na(tp=None) == -1
+    assert na(u=None) == -1
+    assert na(n=None) == -1
+    assert na(B=-1) == -1
+    assert na(u=ctypes.c_void_p(0x10001)) == -1
+    assert na(V=600000) == -4
+    assert na(B=0) == 0
+    assert sv.sv_workspace_size(1024, 8, 128256, True) <= sv.SV_SCRATCH_BYTES
+    assert sv.sv_workspace_size(1024, 16, 128256, True) > sv.SV_SCRATCH_BYTES
+    assert na(B=1024, K=16, V=128256) == -5
+    assert "SCRATCH" in sv.sv_status_string(-5)
+
+
+def test_scratch_size_matches_header():
+    import speculative_decoding_verification_row_amd as sv
+    text = open(HEADER).read()
+    m = re.search(r"#define SV_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == sv.SV_SCRATCH_BYTES
