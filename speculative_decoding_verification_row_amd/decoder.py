@@ -37,10 +37,13 @@ forced_alpha (benchmark only, as the llms-explorer post's forced-acceptance
 ceilings): the drafts and the verification run for real, then the accepted
 prefix is replaced by a run of Bernoulli(forced_alpha) successes drawn from
 the decoder's generator, followed by the argmax of the target row after it.
-The output is then not a decoding of the target.
+That argmax is the library's own (lowest index on ties): a forcing round asks
+its verification call for the row statistics, whose argmax field holds every
+target row's.  The output is then not a decoding of the target.
 
 The verification itself always runs in the library's HIP kernels; `verify`
-replaces it only for tests that exercise this host protocol without a GPU.
+replaces it only for tests that exercise this host protocol without a GPU
+(in a forcing round the hook also returns every target row's argmax).
 """
 from __future__ import annotations
 
@@ -51,7 +54,7 @@ from typing import Callable, List, Optional, Sequence
 import numpy as np
 import torch
 
-from . import sv_verify_greedy_batched, sv_verify_sample_early_batched, workspace_for
+from . import sv_verify_greedy_batched, sv_verify_sample_batched, sv_verify_sample_early_batched, workspace_for
 
 
 @dataclass
@@ -141,7 +144,8 @@ class SpeculativeDecoder:
     governor  -- a Governor (per sequence, reset by every generate call).
     forced_alpha -- benchmark only: force the accepted prefix (see above).
     verify    -- test hook: callable(tp, dp, tokens, uniforms) -> (n, next)
-                 on numpy arrays of one round, replacing the library call.
+                 on numpy arrays of one round, replacing the library call;
+                 with forced_alpha it returns (n, next, argmax [b, k+1]).
     """
 
     def __init__(self, draft_step: Callable, target_step: Callable, k: int = 4, greedy: bool = True,
@@ -187,9 +191,11 @@ class SpeculativeDecoder:
             V = tp.shape[-1]
             dp = None if self.greedy else (np.zeros((b, 0, V), np.float32) if k == 0 else
                                            np.asarray(torch.as_tensor(dprobs).cpu(), np.float32).reshape(b, k, V))
-            n, nx = self.verify(tp, dp, tk, u)
-            am = np.argmax(tp, axis=-1) if forcing else None
-            return np.asarray(tk), np.asarray(n), np.asarray(nx), am
+            res = self.verify(tp, dp, tk, u)
+            if forcing and len(res) != 3:
+                raise ValueError("with forced_alpha the verify hook returns (n, next, row argmax)")
+            am = np.asarray(res[2]).reshape(b, k + 1) if forcing else None
+            return np.asarray(tk), np.asarray(res[0]), np.asarray(res[1]), am
         dev = self._device()
         tp = torch.as_tensor(tprobs, device=dev)
         V = tp.shape[-1]
@@ -200,22 +206,28 @@ class SpeculativeDecoder:
         stream, ws = bufs["stream"], bufs["ws"]
         o = b * k
         dev_out, host_out = bufs["dev"], bufs["host"]
+        st = bufs.get("stats")   # forcing: every target row's argmax, from the row statistics
         if self.greedy:
             sv_verify_greedy_batched(tp, tk, n_accepted=bufs["n"], next_token=bufs["x"], workspace=ws,
-                                     stream=stream)
+                                     stats=st, stream=stream)
         else:
             dp = (torch.zeros((b, 0, V), dtype=torch.float32, device=dev) if k == 0 else
                   _as_f32(dprobs, dev, (b, k, V)))
             bufs["u_host"][...] = u
             bufs["u_dev"].copy_(bufs["u_pin"], non_blocking=True)
-            # the early exit: the full pass's outputs, bit for bit, reading
-            # only the rows they depend on (the driver takes no statistics)
-            sv_verify_sample_early_batched(tp, dp, tk, bufs["u_dev"], n_accepted=bufs["n"], next_token=bufs["x"],
-                                           workspace=ws, stream=stream)
+            if forcing:
+                sv_verify_sample_batched(tp, dp, tk, bufs["u_dev"], n_accepted=bufs["n"], next_token=bufs["x"],
+                                         workspace=ws, stats=st, stream=stream)
+            else:
+                # the early exit: the full pass's outputs, bit for bit,
+                # reading only the rows they depend on
+                sv_verify_sample_early_batched(tp, dp, tk, bufs["u_dev"], n_accepted=bufs["n"],
+                                               next_token=bufs["x"], workspace=ws, stream=stream)
         if host_toks is None:
             dev_out[:o].copy_(tk.reshape(-1))
         if forcing:
-            dev_out[o + 2 * b:].copy_(torch.argmax(tp, dim=-1).to(torch.int32).reshape(-1))
+            # the argmax field (the first int32 of each 48-byte sv_row_stats)
+            dev_out[o + 2 * b:].copy_(st.view(torch.int32).reshape(b, k + 1, 12)[:, :, 0].reshape(-1))
         # one transfer back into pinned memory, then wait for the round's work
         host_out.copy_(dev_out, non_blocking=True)
         stream.synchronize()
@@ -232,8 +244,8 @@ class SpeculativeDecoder:
     def _buffers(self, dev, b: int, k: int, V: int, forcing: bool) -> dict:
         """Per (device, stream, b, k, V): a device int32 buffer for the
         round's tokens, n, next (and argmaxes) with views of n and next, its
-        pinned host mirror, pinned and device uniforms, the stream and the
-        verification workspace."""
+        pinned host mirror, pinned and device uniforms, the stream, the
+        verification workspace and, when forcing, the row statistics."""
         stream = torch.cuda.current_stream(dev)
         key = (dev.index, stream.cuda_stream, b, k, V, forcing)
         bufs = self._bufcache.get(key)
@@ -246,6 +258,8 @@ class SpeculativeDecoder:
                     "u_dev": torch.empty((b, k + 1), dtype=torch.float32, device=dev),
                     "stream": stream,
                     "ws": workspace_for(b, k, V, not self.greedy, dev, stream)}
+            if forcing:
+                bufs["stats"] = torch.empty((b, k + 1, 48), dtype=torch.uint8, device=dev)
             bufs["n"], bufs["x"] = bufs["dev"][o:o + b], bufs["dev"][o + b:o + 2 * b]
             bufs["host_np"] = bufs["host"].numpy()
             bufs["u_host"] = bufs["u_pin"].numpy()

@@ -41,6 +41,18 @@ class HashLM:
         return self._row(tuple(int(t) for t in ctx))
 
 
+class TiedLM(HashLM):
+    """HashLM whose every row copies its maximum to a second, seeded index:
+    an exact two-way tie for the argmax (rows are then not normalised, which
+    the verifier allows)."""
+
+    def _row_uncached(self, ctx: tuple) -> np.ndarray:
+        r = super()._row_uncached(ctx).copy()
+        g = np.random.default_rng([self.salt + 7919, _ctx_key(ctx)])
+        r[int(g.integers(0, self.V))] = r.max()
+        return r
+
+
 def greedy_decode(model: HashLM, prompt, max_new: int):
     seq = list(prompt)
     for _ in range(max_new):

@@ -13,7 +13,7 @@ import speculative_decoding_verification_row_amd as sv
 from speculative_decoding_verification_row_amd import SpeculativeDecoder
 from speculative_decoding_verification_row_amd.decoder import Governor
 
-from _models import HashLM, greedy_decode, make_callbacks
+from _models import HashLM, TiedLM, greedy_decode, make_callbacks
 from test_decoder_host import oracle_verify, sampled_law_check
 
 pytestmark = pytest.mark.gpu
@@ -144,3 +144,29 @@ def test_gpu_random_decoder_configs(j):
     if greedy:
         want = [greedy_decode(target, p, max_new) for p in prompts]
         assert (outs[0] if batched else [outs[0]]) == want
+
+
+@pytest.mark.parametrize("alpha", [0.3, 0.6, 0.85])
+def test_gpu_forced_acceptance_matches_oracle_driver(alpha):
+    """Forced acceptance at 0 < alpha < 1: the token after the forced prefix
+    is the library's lowest-index argmax of that target row (from the row
+    statistics of the round's verification call).  Target rows with an exact
+    two-way tie for the maximum make the tie rule matter.  The streams equal
+    those of the oracle-driven driver (the oracle's row statistics supply the
+    argmax), greedy and sampled, batched and not."""
+    for greedy in (True, False):
+        for batched in (False, True):
+            _case(f"forced acceptance alpha={alpha} greedy={greedy} batched={batched}, V=3000 tied rows")
+            target = TiedLM(3000, sigma=2.0, salt=81)
+            draft = HashLM(3000, salt=82, base=target, noise=1.0)
+            prompts = [[3, 1], [4], [5, 9, 2]] if batched else [[3, 1]]
+            outs, accepted = [], []
+            for verify in (None, oracle_verify(greedy)):
+                ds, ts = make_callbacks(target, draft, greedy=greedy, seed=13, batched=batched)
+                dec = SpeculativeDecoder(ds, ts, k=4, greedy=greedy, seed=14, batched=batched, verify=verify,
+                                         forced_alpha=alpha)
+                outs.append(dec.generate(prompts if batched else prompts[0], max_new=30))
+                accepted.append(list(dec.stats.accepted))
+            assert outs[0] == outs[1]
+            assert accepted[0] == accepted[1]
+            assert 0 < np.mean(accepted[0]) < 4

@@ -12,13 +12,16 @@ import oracle
 from speculative_decoding_verification_row_amd import SpeculativeDecoder
 from speculative_decoding_verification_row_amd.decoder import Governor
 
-from _models import HashLM, greedy_decode, make_callbacks
+from _models import HashLM, TiedLM, greedy_decode, make_callbacks
 
 
 def oracle_verify(greedy):
+    """The oracle as the decoder's verification hook; it also returns every
+    target row's argmax (the oracle's row statistics), which forcing rounds
+    use."""
     def f(tp, dp, tk, u):
         o = oracle.verify_greedy(tp, tk) if greedy else oracle.verify_sample(tp, dp, tk, u)
-        return o["n_accepted"], o["next_token"]
+        return o["n_accepted"], o["next_token"], o["stats"]["argmax"]
     return f
 
 
@@ -208,3 +211,14 @@ def test_forced_acceptance():
     assert abs(dec.stats.acceptance_fraction() - want) < 4 * se
     with pytest.raises(ValueError):
         SpeculativeDecoder(ds, ts, forced_alpha=1.5)
+    # the forced token is the lowest-index argmax: with exact ties in every
+    # target row, alpha = 0 is still plain greedy decoding (numpy.argmax)
+    tied = TiedLM(40, sigma=2.0, salt=19)
+    ds, ts = make_callbacks(tied, HashLM(40, salt=20, base=tied, noise=2.0), greedy=False, seed=2)
+    dec = SpeculativeDecoder(ds, ts, k=3, greedy=False, seed=8, verify=oracle_verify(False), forced_alpha=0.0)
+    assert dec.generate([5], max_new=25) == greedy_decode(tied, [5], 25)
+    # a verify hook without the argmax is refused in a forcing round
+    dec = SpeculativeDecoder(ds, ts, k=3, greedy=True, forced_alpha=0.5,
+                             verify=lambda tp, dp, tk, u: oracle_verify(True)(tp, dp, tk, u)[:2])
+    with pytest.raises(ValueError):
+        dec.generate([5], max_new=5)
