@@ -20,7 +20,9 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libsv_oracle.so")
+# SV_ORACLE_LIB selects another build of the same source (the sanitizer
+# build of oracle/build.py --sanitize).
+_LIB_PATH = os.environ.get("SV_ORACLE_LIB") or os.path.join(_HERE, "libsv_oracle.so")
 
 ROW_STATS_DTYPE = np.dtype([
     ("argmax", np.int32), ("max_p", np.float32),
