@@ -1,7 +1,7 @@
 """Benchmark of the batched verification step on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
-                    [--mode sampled|greedy] [--no-cpu-baseline]
+                    [--mode sampled|greedy] [--no-cpu-baseline] [--no-ceiling]
 
 One step = one call of the verification library over a whole batch (all
 rows of all B sequences: the fused row pass, the acceptance decisions, the
@@ -13,8 +13,9 @@ sets alternate so that consecutive steps never hit the same data in the
 Printed: one JSON line (rank 0) with verify rounds/s as `value`, the
 roofline of the dominant kernel (formula bytes per launch over the average
 launch duration, from one pair of HIP events on the launch stream around the
-timed launches, against 8 TB/s), and the fp64
-CPU oracle timed on the host's cores on a bounded sample of the same
+timed launches, against 8 TB/s), the empirical ceiling of a plain read of
+the same bytes on this GPU (context), and the fp64 CPU oracle timed on one
+host thread and on the host's cores over a bounded sample of the same
 workload.
 """
 import argparse
@@ -65,30 +66,34 @@ def traffic_for(kernel: str, workload: str):
     return e.get("bytes_per_launch")
 
 
-def cpu_baseline(cfg, mode, target_seconds=10.0, logits=False, tau=1.0):
-    """Time the fp64 oracle as it stands on this host's cores over a bounded
-    sample of the workload (whole sequences of round 0), scaled to rounds/s.
-    The logits oracle is numpy on one thread."""
-    import numpy as np
-    import oracle
-    import workloads
-    cores = 1 if logits else workloads.default_workers()
-    B = cfg["B"]
-    n_seq = min(B, max(1, 2 * cores))
-    seqs = list(range(n_seq))
-    hb = workloads.make_batch(cfg["family"], B, cfg["K"], cfg["V"], seed=0, seqs=seqs, logits=logits)
-    sampled = mode == "sampled"
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
-    def once():
-        if logits:
-            from oracle.logits import verify_sample_logits
-            verify_sample_logits(hb.target_probs, hb.draft_probs, hb.draft_tokens, hb.uniforms, tau)
-        elif sampled:
-            oracle.verify_sample(hb.target_probs, hb.draft_probs, hb.draft_tokens, hb.uniforms,
-                                 threads=cores, diagnostics=False)
-        else:
-            oracle.verify_greedy(hb.target_probs, hb.draft_tokens, threads=cores)
 
+def cpu_threads() -> tuple:
+    """(threads the multi-threaded oracle run uses, CPUs in this process's
+    affinity mask).  The threads are the affinity mask's CPUs, capped by the
+    host's CPU share for this process when OMP_NUM_THREADS states one (a
+    shared GPU host gives each GPU a share of its cores)."""
+    try:
+        n_aff = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n_aff = os.cpu_count() or 1
+    share = os.environ.get("OMP_NUM_THREADS", "")
+    n = n_aff
+    if share.isdigit() and int(share) > 0:
+        n = min(n, int(share))
+    return max(1, n), n_aff
+
+
+def _time_oracle(once, target_seconds):
     once()
     reps, t0 = 0, time.perf_counter()
     while True:
@@ -96,11 +101,100 @@ def cpu_baseline(cfg, mode, target_seconds=10.0, logits=False, tau=1.0):
         reps += 1
         el = time.perf_counter() - t0
         if el >= target_seconds:
-            break
-    seq_per_s = reps * n_seq / el
-    return {"value": seq_per_s / B, "unit": "rounds/s", "cores": cores, "kind": "oracle",
-            "sample": f"{n_seq} of {B} sequences of round 0, repeated {reps}x in {el:.1f}s, "
-                      f"scaled by {n_seq}/{B} to whole rounds"}
+            return reps, el
+
+
+def cpu_baseline(cfg, mode, target_seconds=10.0, logits=False, tau=1.0):
+    """Time the fp64 oracle as it stands over a bounded sample of the
+    workload (whole sequences of round 0), scaled to rounds/s: once on one
+    thread and once on the host's cores (cpu_threads; the oracle splits a
+    batch over threads by whole sequences).  The logits oracle is numpy on
+    one thread, so it is timed once."""
+    import oracle
+    import workloads
+    B = cfg["B"]
+    threads, n_aff = cpu_threads()
+    if logits:
+        threads = 1
+    n_seq = min(B, max(1, 2 * threads))
+    hb = workloads.make_batch(cfg["family"], B, cfg["K"], cfg["V"], seed=0, seqs=list(range(n_seq)), logits=logits)
+    sampled = mode == "sampled"
+
+    def run(nthreads, seqs):
+        sl = slice(0, seqs)
+        args = (hb.target_probs[sl], hb.draft_probs[sl] if sampled or logits else None, hb.draft_tokens[sl],
+                hb.uniforms[sl])
+
+        def once():
+            if logits:
+                from oracle.logits import verify_sample_logits
+                verify_sample_logits(args[0], args[1], args[2], args[3], tau)
+            elif sampled:
+                oracle.verify_sample(*args, threads=nthreads, diagnostics=False)
+            else:
+                oracle.verify_greedy(args[0], args[2], threads=nthreads)
+        reps, el = _time_oracle(once, target_seconds)
+        return reps * seqs / el / B, f"{seqs} of {B} sequences of round 0, repeated {reps}x in {el:.1f}s " \
+                                     f"on {nthreads} thread(s), scaled by {seqs}/{B} to whole rounds"
+
+    v1, s1 = run(1, min(n_seq, 2))
+    out = {"value": v1, "unit": "rounds/s", "cores": 1, "kind": "oracle", "sample": s1,
+           "cpu_model": cpu_model(), "affinity_cpus": n_aff}
+    if threads > 1:
+        vn, sn = run(threads, n_seq)
+        out.update(value=vn, cores=threads, sample=sn, single_thread={"value": v1, "sample": s1})
+    return out
+
+
+def stream_ceiling(sets, sampled, steps=20):
+    """The empirical ceiling of one read pass on this GPU: the streaming-read
+    probe (libsv_probe.so; no arithmetic but a keep-alive sum) over the same
+    operand bytes as a step, in both launch shapes (one block per 32 KB
+    chunk, and one persistent block per CU), two input sets alternating, one
+    pair of HIP events around the timed launches.  Context for the roofline,
+    never its peak."""
+    import ctypes
+    import torch
+    path = os.path.join(ROOT, "speculative_decoding_verification_row_amd", "libsv_probe.so")
+    if not os.path.exists(path):
+        return {"note": "libsv_probe.so not built"}
+    L = ctypes.CDLL(path)
+    P, SZ, I32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
+    L.sv_probe_blocks.argtypes = [SZ, SZ, I32, I32]
+    L.sv_probe_blocks.restype = ctypes.c_int64
+    L.sv_probe_read.argtypes = [P, SZ, P, SZ, I32, I32, P, P]
+    L.sv_probe_read.restype = I32
+    bufs = []
+    for db in sets:
+        t, d = db["tp"], db["dp"] if sampled else None
+        bufs.append((t.data_ptr(), t.numel() * 4, d.data_ptr() if d is not None else None,
+                     d.numel() * 4 if d is not None else 0))
+    b0, b1 = bufs[0][1], bufs[0][3]
+    stream = torch.cuda.current_stream()
+    out = {"bytes_per_launch": b0 + b1, "unit": "GB/s", "steps": steps}
+    for name, mode, bpc in (("one_shot", 0, 0), ("persistent", 1, 1)):
+        nb = L.sv_probe_blocks(b0, b1, mode, bpc)
+        res = torch.empty(max(nb, 1), dtype=torch.float32, device=sets[0]["tp"].device)
+
+        def launch(k):
+            x = bufs[k % len(bufs)]
+            rc = L.sv_probe_read(x[0], x[1], x[2], x[3], mode, bpc, res.data_ptr(), stream.cuda_stream)
+            assert rc == 0, f"probe launch failed ({rc})"
+        for k in range(4):
+            launch(k)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for k in range(steps):
+            launch(k)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        out[name] = {"us": round(us, 2), "gbs": round((b0 + b1) / us / 1e3, 1)}
+    best = max(out["one_shot"]["gbs"], out["persistent"]["gbs"])
+    out["gbs"] = best
+    out["frac_of_peak"] = round(best / PEAK_HBM_GBS, 4)
+    return out
 
 
 def main():
@@ -118,11 +212,16 @@ def main():
     ap.add_argument("--logits", action="store_true",
                     help="sampled verification given logits (warped in the library) instead of probabilities")
     ap.add_argument("--temperature", type=float, default=1.0, help="temperature of --logits")
+    ap.add_argument("--stats", action="store_true",
+                    help="sampled or greedy verification that also writes the per-row statistics (argmax, max, "
+                         "sum p, sum q, sum min, sum max(0, p - q), p(t), q(t)): the full fused pass")
     ap.add_argument("--early-exit", action="store_true",
                     help="sampled verification through the early-exit entry point (reads only the rows the "
                          "outputs depend on; its byte count is those rows)")
     ap.add_argument("--decoder", action="store_true",
                     help="time rounds of the multi-round driver (B=1, K=4, V=32000) instead")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the streaming-read probe (the empirical ceiling reported beside the roofline)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy 5 times (reference for "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE scaling)")
@@ -154,22 +253,28 @@ def main():
     sampled = mode == "sampled"
     if args.early_exit and not sampled:
         raise SystemExit("--early-exit takes the sampled mode (probabilities or --logits)")
+    if args.stats and (args.logits or args.early_exit):
+        raise SystemExit("--stats takes the probability passes (the logits and early-exit passes write none)")
     B, K, V = cfg["B"], cfg["K"], cfg["V"]
     dev = torch.device("cuda:0")
     workload = f"B={B} K={K} V={V} {mode}" + (f" logits tau={args.temperature:g}" if args.logits else "")
     if args.early_exit:
         workload += " early-exit"
+    if args.stats:
+        workload += " stats"
     log(f"workload {args.workload}: {workload}; generating {args.sets} input sets")
 
     sets = []
     for s in range(args.sets):
         sets.append(device_batch(cfg["family"], B, K, V, seed=s, device=dev, sampled=sampled,
-                                 workers=args.gen_workers, logits=args.logits))
+                                 workers=args.gen_workers, logits=args.logits,
+                                 progress=lambda d, n: log(f"    {d}/{n} sequences")))
         log(f"  set {s} ready ({sets[-1]['sha256'][:12]})")
     n_out = torch.empty(B, dtype=torch.int32, device=dev)
     x_out = torch.empty(B, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream(dev)
     ws = sv.workspace_for(B, K, V, sampled, dev, stream)
+    st_out = torch.empty((B, K + 1, 48), dtype=torch.uint8, device=dev) if args.stats else None
 
     def step(db):
         if args.logits:
@@ -181,10 +286,10 @@ def main():
                                               next_token=x_out, workspace=ws, stream=stream)
         elif sampled:
             sv.sv_verify_sample_batched(db["tp"], db["dp"], db["dt"], db["u"], n_accepted=n_out,
-                                        next_token=x_out, workspace=ws, stream=stream)
+                                        next_token=x_out, workspace=ws, stats=st_out, stream=stream)
         else:
             sv.sv_verify_greedy_batched(db["tp"], db["dt"], n_accepted=n_out, next_token=x_out,
-                                        workspace=ws, stream=stream)
+                                        workspace=ws, stats=st_out, stream=stream)
 
     for w in range(args.warmup):
         step(sets[w % len(sets)])
@@ -210,7 +315,7 @@ def main():
     # spot check of the last step's outputs against the oracle (2 sequences)
     last = sets[(args.steps - 1) % len(sets)]
     spot = spot_check(cfg, mode, last, n_out, x_out, seed=(args.steps - 1) % len(sets),
-                      logits=args.logits, tau=args.temperature)
+                      logits=args.logits, tau=args.temperature, stats=st_out)
 
     fbytes = workloads.formula_bytes(B, K, V, sampled)
     formula = fbytes
@@ -265,6 +370,12 @@ def main():
             torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
         line["copy_calibration_bytes"] = src.numel() * 4
+    if not args.no_ceiling:
+        log("streaming-read probe over the same bytes (empirical ceiling, context)")
+        ceil = stream_ceiling(sets, sampled)
+        if "gbs" in ceil:
+            ceil["kernel_frac_of_ceiling"] = round(achieved / ceil["gbs"], 4)
+        line["stream_ceiling"] = ceil
     if not args.no_cpu_baseline:
         log("timing the CPU oracle baseline")
         line["cpu_baseline"] = cpu_baseline(cfg, mode, logits=args.logits, tau=args.temperature)
@@ -347,7 +458,9 @@ def decoder_bench(args):
     print(json.dumps(line), flush=True)
 
 
-def spot_check(cfg, mode, db, n_out, x_out, seed, logits=False, tau=1.0):
+def spot_check(cfg, mode, db, n_out, x_out, seed, logits=False, tau=1.0, stats=None):
+    """Two sequences of the last step against the oracle (and, with row
+    statistics, their masses and argmax)."""
     import numpy as np
     import oracle
     import workloads
@@ -371,6 +484,13 @@ def spot_check(cfg, mode, db, n_out, x_out, seed, logits=False, tau=1.0):
     if not np.all(ok | bnd):
         raise SystemExit(f"benchmark outputs differ from the oracle: gpu {n},{x} oracle "
                          f"{o['n_accepted']},{o['next_token']}")
+    if stats is not None:
+        import speculative_decoding_verification_row_amd as sv
+        g = sv.stats_to_numpy(stats)[seqs]
+        ref = o["stats"]
+        if not (np.array_equal(g["argmax"], ref["argmax"]) and
+                float(np.max(np.abs(g["sum_p"] - ref["sum_p"]) / ref["sum_p"])) <= 1e-9):
+            raise SystemExit("benchmark row statistics differ from the oracle")
     return f"{int(ok.sum())}/{len(seqs)} sequences identical to the oracle ({int(bnd.sum())} boundary)"
 
 

@@ -203,3 +203,34 @@ def test_scratch_size_matches_header():
     text = open(HEADER).read()
     m = re.search(r"#define SV_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
     assert m and int(m.group(1)) << int(m.group(2)) == sv.SV_SCRATCH_BYTES
+
+
+PROBE_HEADER = os.path.join(ROOT, "include", "sv_probe.h")
+
+
+def test_probe_library_exports_its_header_and_checks_arguments():
+    """libsv_probe.so (the streaming-read probe the benchmark reports as
+    context) exports what include/sv_probe.h declares; chunk counts and
+    argument errors need no GPU."""
+    import speculative_decoding_verification_row_amd as sv
+    from speculative_decoding_verification_row_amd import build
+    path = build.PROBE_LIB
+    if not os.path.exists(path):
+        build.build()
+    text = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(sv_[a-z_]+)\s*\(", text)))
+    assert names == ["sv_probe_blocks", "sv_probe_read"]
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (sv_[a-z_]+)$", out, flags=re.M))
+    assert set(names) <= exported
+    L = ctypes.CDLL(path)
+    L.sv_probe_blocks.argtypes = [ctypes.c_size_t, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int32]
+    L.sv_probe_blocks.restype = ctypes.c_int64
+    L.sv_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t,
+                                ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    assert L.sv_probe_blocks(32768, 32768 + 16, 0, 0) == 3      # one block per started 32 KB chunk
+    assert L.sv_probe_blocks(16, 0, 7, 1) == -1                   # unknown mode
+    assert L.sv_probe_read(None, 16, None, 0, 0, 0, FAKE, None) == -1
+    assert L.sv_probe_read(FAKE, 24, None, 0, 0, 0, FAKE, None) == -1        # size not a multiple of 16
+    assert L.sv_probe_read(FAKE, 16, None, 16, 0, 0, FAKE, None) == -1       # second buffer missing
+    assert L.sv_probe_read(ctypes.c_void_p(0x10008), 16, None, 0, 0, 0, FAKE, None) == -1   # misaligned

@@ -45,3 +45,32 @@ def test_traffic_only_for_the_current_code(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "absent.json"))
     assert bench.traffic_for("kern", "wl") is None
 
+
+
+def test_cpu_threads_follow_affinity_and_share(monkeypatch):
+    import os
+    n_aff = len(os.sched_getaffinity(0))
+    monkeypatch.delenv("OMP_NUM_THREADS", raising=False)
+    assert bench.cpu_threads() == (n_aff, n_aff)
+    monkeypatch.setenv("OMP_NUM_THREADS", "1")
+    assert bench.cpu_threads() == (1, n_aff)
+    monkeypatch.setenv("OMP_NUM_THREADS", str(n_aff + 100))
+    assert bench.cpu_threads() == (n_aff, n_aff)
+
+
+def test_cpu_model_is_named():
+    assert isinstance(bench.cpu_model(), str) and bench.cpu_model()
+
+
+def test_cpu_baseline_reports_single_and_multi_thread(monkeypatch):
+    """A tiny workload so the timing loop ends at once: both figures and the
+    fields the benchmark line carries are there."""
+    monkeypatch.setenv("OMP_NUM_THREADS", "2")
+    cfg = dict(family="c3", B=4, K=2, V=300)
+    r = bench.cpu_baseline(cfg, "sampled", target_seconds=0.05)
+    assert r["kind"] == "oracle" and r["unit"] == "rounds/s" and r["value"] > 0
+    assert r["cpu_model"] and r["affinity_cpus"] >= 1
+    if r["cores"] > 1:
+        assert r["single_thread"]["value"] > 0
+    g = bench.cpu_baseline(dict(family="c2", B=4, K=2, V=300), "greedy", target_seconds=0.05)
+    assert g["value"] > 0

@@ -16,6 +16,7 @@ import speculative_decoding_verification_row_amd as sv
 from _parity import check_sampled
 from test_gpu_parity import SMALL, _random_rows
 from test_gpu_random_shapes import _shape, _rows
+from _forms import FORMS, set_form
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -34,9 +35,9 @@ def _need_gpu():
     torch.cuda.synchronize()
 
 
-@pytest.fixture(params=["walks", "rows"])
+@pytest.fixture(params=FORMS)
 def form(request, monkeypatch):
-    monkeypatch.setenv("SV_VERIFY_ROWS", "1" if request.param == "rows" else "0")
+    set_form(monkeypatch, request.param)
     return request.param
 
 

@@ -1,6 +1,6 @@
 """GPU parity of the two rarely taken paths of the sampled passes, through
-the C ABI, in both forms (walks, one block per draft row) and every sampled
-entry point (probabilities with and without row statistics, early exit,
+the C ABI, in both forms of the pass (walks, one block per draft row) and
+every sampled entry point (probabilities with and without row statistics, early exit,
 logits, logits with early exit).
 
 1. The zero-residual fallback (R8; the spec-verify kernel card, section
@@ -30,6 +30,7 @@ from oracle.logits import verify_sample_logits
 import speculative_decoding_verification_row_amd as sv
 
 from _parity import BAND_LOGITS, boundary_mask, check_logits, check_sampled
+from _forms import FORMS, set_form
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -50,9 +51,9 @@ def _need_gpu():
     torch.cuda.synchronize()
 
 
-@pytest.fixture(params=["walks", "rows"])
+@pytest.fixture(params=FORMS)
 def form(request, monkeypatch):
-    monkeypatch.setenv("SV_VERIFY_ROWS", "1" if request.param == "rows" else "0")
+    set_form(monkeypatch, request.param)
     return request.param
 
 

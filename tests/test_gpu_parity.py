@@ -17,6 +17,7 @@ from workloads.device import device_batch
 import speculative_decoding_verification_row_amd as sv
 
 from _parity import BAND_PROB, FP64_RTOL, check_greedy, check_sampled
+from _forms import FORMS, set_form
 
 pytestmark = pytest.mark.gpu
 
@@ -96,10 +97,10 @@ STATS = [True, False]
 
 # Both forms of the sampled pass: walks down the draft rows, and one block per
 # draft row (which the library picks by itself when every block fits on the
-# chip at once).  SV_VERIFY_ROWS forces one or the other.
-@pytest.fixture(params=["walks", "rows"])
+# chip at once).
+@pytest.fixture(params=FORMS)
 def form(request, monkeypatch):
-    monkeypatch.setenv("SV_VERIFY_ROWS", "1" if request.param == "rows" else "0")
+    set_form(monkeypatch, request.param)
     return request.param
 
 

@@ -15,6 +15,7 @@ from oracle.logits import verify_sample_logits
 import speculative_decoding_verification_row_amd as sv
 
 from _parity import BAND_PROB, check_greedy, check_logits, check_sampled, compare_outputs
+from _forms import set_form
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -89,7 +90,7 @@ def test_random_shape(j, monkeypatch):
     stats = bool(j % 2)
     form = FORMS[j % 3]
     if form != "auto":
-        monkeypatch.setenv("SV_VERIFY_ROWS", "1" if form == "rows" else "0")
+        set_form(monkeypatch, form)
     _case(f"random shape {j}: B={B} K={K} V={V} stats={stats} sampled form={form}")
     p, q, t, u = _rows(rng, B, K, V)
     tp, dp, dt, ud = _dev(p, q, t, u)

@@ -11,10 +11,11 @@ from . import CONFIGS, iter_sequences, default_workers
 
 def device_batch(family: str, B: int, K: int, V: int, seed: int = 0, rnd: int = 0,
                  device="cuda", workers: int | None = None, sampled: bool = True,
-                 keep_host=None, logits: bool = False):
+                 keep_host=None, logits: bool = False, progress=None):
     """Return dict(tp, dp, dt, u) of device tensors plus 'info' (per-sequence
     generator info) and 'sha256' of the host bytes.  keep_host: optional set
-    of sequence indices whose host arrays are also returned in 'host'."""
+    of sequence indices whose host arrays are also returned in 'host'.
+    progress: optional callable(done, B), called every 128 sequences."""
     import torch
     workers = default_workers() if workers is None else workers
     tp = torch.empty((B, K + 1, V), dtype=torch.float32, device=device)
@@ -42,6 +43,8 @@ def device_batch(family: str, B: int, K: int, V: int, seed: int = 0, rnd: int = 
         infos[b] = info
         if keep_host is not None and b in keep_host:
             host[b] = (p, q, t, uu)
+        if progress is not None and (b + 1) % 128 == 0:
+            progress(b + 1, B)
     h.update(dt.tobytes())
     h.update(u.tobytes())
     return {
