@@ -336,9 +336,9 @@ __device__ __forceinline__ void acc_f4(Acc& a, float4 p4, float4 q4, int k)
         }
         if constexpr ((M & kSP) != 0) a.sp += (double)p;
         if constexpr ((M & (kSQ | kSMIN)) != 0) {
-            const float q = comp(q4, e);
-            if constexpr ((M & kSQ) != 0) a.sq += (double)q;
-            if constexpr ((M & kSMIN) != 0) a.smin += (double)fminf(p, q);
+            const double qd = (double)comp(q4, e);
+            if constexpr ((M & kSQ) != 0) a.sq += qd;
+            if constexpr ((M & kSMIN) != 0) a.smin += __builtin_fmin((double)p, qd);
         }
     }
 }
@@ -570,9 +570,18 @@ struct Gathered {
 // whose decision is pending (target float4s, then draft float4s; each thread
 // touches only its own column, so no barrier guards it); when it finishes a
 // sequence, the gathered partials.
+// The partials of several rows of one sequence, entry r * NC + c for row r
+// of the tile and chunk c.
+struct FlatGathered {
+    static constexpr int kCap = kGroup * kMaxNC;
+    double sp[kCap], sq[kCap], smin[kCap];
+    unsigned long long am[kCap];
+};
+
 union SampleLds {
     f32x4 parked[2 * kVecS][kThreads];
     Gathered<kMaxNC> g;
+    FlatGathered f;
 };
 __shared__ SampleLds lds;
 // The greedy kernel's rows have at most SV_MAX_V / kChunkG chunks.
@@ -869,11 +878,11 @@ struct Outcome {
 
 // Block-cooperative, run by the finishing block of sequence b after its walk:
 // combine the rows of sequence b in groups of kGroup (wave w takes row
-// g0 + w), take the decisions and, when requested, write the row statistics;
-// without statistics it stops after the group that holds the first
+// g0 + w), take the decisions and, when `write` is set, write the row
+// statistics; without it it stops after the group that holds the first
 // rejection.  Uniform result.
 template <bool VEC, bool SAMPLED, int NV, int MROW, int MLAST, class G>
-__device__ Outcome finish_rows(G& g, const Args& a, int b)
+__device__ Outcome finish_rows(G& g, const Args& a, int b, bool write)
 {
     __shared__ int s_rej[kGroup], s_arg[kGroup];
     __shared__ double s_P[kGroup], s_Q[kGroup];
@@ -903,7 +912,7 @@ __device__ Outcome finish_rows(G& g, const Args& a, int b)
                 } else {
                     rej = (i < K && tk != rv.arg) ? 1 : 0;
                 }
-                if (a.stats) write_stats(a, row, rv, pair, pt, qt, i < K);
+                if (write) write_stats(a, row, rv, pair, pt, qt, i < K);
                 s_rej[w] = rej;
                 s_P[w] = rv.P;
                 s_Q[w] = rv.Q;
@@ -922,9 +931,138 @@ __device__ Outcome finish_rows(G& g, const Args& a, int b)
             }
         }
         __syncthreads();
-        if (done && !a.stats) break;
+        if (done && !write) break;
     }
     return o;
+}
+
+// Block-cooperative: the partials of rows row0 .. row0 + nrows - 1 of sequence
+// b into f (fields MROW of rows below K, MLAST of row K), nrows * NC <=
+// FlatGathered::kCap.  Partials that do not carry this call's tag within the
+// wait bound are recomputed from the inputs (as gather_rows does).
+template <bool VEC, int MROW, int MLAST>
+__device__ void gather_flat(FlatGathered& f, const Args& a, int b, int row0, int nrows)
+{
+    constexpr int kPer = FlatGathered::kCap / kThreads;
+    const int NC = a.NC, K = a.K, V = a.V;
+    const unsigned ep = a.epoch;
+    const int n_ent = nrows * NC;
+    bool need[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) need[j] = (int)threadIdx.x + j * kThreads < n_ent;
+    const unsigned long long t0 = wall_clock64();
+    for (;;) {
+        bool any = false;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            if (!need[j]) continue;
+            const int e = (int)threadIdx.x + j * kThreads, r = e / NC, c = e - r * NC;
+            const int i = row0 + r;
+            const Part* pp = &a.parts[((int64_t)b * (K + 1) + i) * NC + c];
+            const int M = i < K ? MROW : MLAST;
+            const unsigned long long wsp = get_u64(&pp->sp);
+            const unsigned long long wsq = (M & kSQ) ? get_u64(&pp->sq) : 0ull;
+            const unsigned long long wsm = (M & kSMIN) ? get_u64(&pp->smin) : 0ull;
+            const unsigned long long wam = (M & kAM) ? get_u64(&pp->am) : 0ull;
+            const bool ok = f64_ok(wsp, ep) && (!(M & kSQ) || f64_ok(wsq, ep)) && (!(M & kSMIN) || f64_ok(wsm, ep)) &&
+                            (!(M & kAM) || am_ok(wam, ep));
+            if (ok && !a.force_recompute) {
+                f.sp[e] = f64_of(wsp);
+                f.sq[e] = f64_of(wsq);
+                f.smin[e] = f64_of(wsm);
+                f.am[e] = wam;
+                need[j] = false;
+            } else {
+                any = true;
+            }
+        }
+        if (!__syncthreads_or(any)) return;   // everything arrived (the usual case)
+        if (wait_expired(a, t0)) break;
+        __builtin_amdgcn_s_sleep(2);
+    }
+    // what is still missing (rare): recompute it, one entry at a time
+    __shared__ int s_e;
+    for (int e0 = 0; e0 < n_ent; ++e0) {
+        bool mine = false;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j)
+            if (need[j] && (int)threadIdx.x + j * kThreads == e0) mine = true;
+        if (!__syncthreads_or(mine)) continue;
+        if (mine) s_e = e0;
+        __syncthreads();
+        const int e = s_e, r = e / NC, c = e - r * NC, i = row0 + r;
+        const int64_t row = (int64_t)b * (K + 1) + i;
+        const Row prow = row_of(a.tp + row * V, V);
+        const Row qrow = i < K ? row_of(a.dp + ((int64_t)b * K + i) * V, V) : prow;
+        const Acc st = i < K ? block_reduce<MROW>(thread_stats_reload<VEC, MROW, kVecS>(prow, qrow, c))
+                             : block_reduce<MLAST>(thread_stats_reload<VEC, MLAST, kVecS>(prow, prow, c));
+        if (threadIdx.x == 0) {
+            f.sp[e] = strip8(st.sp);
+            f.sq[e] = strip8(st.sq);
+            f.smin[e] = strip8(st.smin);
+            f.am[e] = tag_am(st.maxv, st.arg, a.epoch);
+            put_u32(&a.hdr->slow_path, 1u);
+        }
+        __syncthreads();
+    }
+}
+
+// Wave-cooperative combine of the tile row whose entries start at `base`
+// (the order of combine_row; values valid in every lane).
+template <int M>
+__device__ __forceinline__ RowView combine_flat(const FlatGathered& f, int base, int NC)
+{
+    const int lane = threadIdx.x & 63;
+    RowView v{0.0, 0.0, 0.0, -INFINITY, INT_MAX};
+    v.P = sum_chunks(&f.sp[base], NC);
+    if constexpr ((M & kSQ) != 0) v.Q = sum_chunks(&f.sq[base], NC);
+    if constexpr ((M & kSMIN) != 0) v.Smin = sum_chunks(&f.smin[base], NC);
+    if constexpr ((M & kAM) != 0) {
+        float mv = -INFINITY;
+        int ai = INT_MAX;
+        for (int h = 0; h < 2; ++h) {
+            const int c = lane + 64 * h;
+            if (c < NC) argmax_merge(mv, ai, am_val(f.am[base + c]), am_arg(f.am[base + c]));
+        }
+        wave_argmax(mv, ai);
+        v.maxv = mv;
+        v.arg = ai;
+    }
+    return v;
+}
+
+// Block-cooperative: the row statistics of every row of sequence b, written
+// by the block that finishes it.  Rows go in tiles of as many rows as the
+// LDS tile holds (all of them for K + 1 <= 512 / NC): thread t loads the
+// draft token of tile row t while the tile's partials are gathered, then
+// that token's values while the waves combine the rows (wave w takes rows w,
+// w + 4, ...), and writes row t's statistics.
+template <bool VEC, int MROW, int MLAST>
+__device__ void write_all_stats(const Args& a, int b)
+{
+    constexpr int kTileMax = 64;
+    __shared__ RowView s_rv[kTileMax];
+    const int NC = a.NC, K = a.K, V = a.V;
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int per_tile = FlatGathered::kCap / NC < kTileMax ? FlatGathered::kCap / NC : kTileMax;
+    for (int r0 = 0; r0 <= K; r0 += per_tile) {
+        const int T = (K + 1 - r0) < per_tile ? (K + 1 - r0) : per_tile;
+        const int i = r0 + t;
+        const int64_t row = (int64_t)b * (K + 1) + i;
+        int tk = -1;
+        if (t < T && i < K) tk = a.dt[(int64_t)b * K + i];
+        gather_flat<VEC, MROW, MLAST>(lds.f, a, b, r0, T);
+        const bool tin = t < T && i < K && tk >= 0 && tk < V;
+        const float pt = tin ? a.tp[row * V + tk] : 0.0f;
+        const float qt = tin ? a.dp[((int64_t)b * K + i) * V + tk] : 0.0f;
+        for (int r = w; r < T; r += kWaves) {
+            const RowView rv = r0 + r < K ? combine_flat<MROW>(lds.f, r * NC, NC) : combine_flat<MLAST>(lds.f, r * NC, NC);
+            if (lane == 0) s_rv[r] = rv;
+        }
+        __syncthreads();
+        if (t < T) write_stats(a, row, s_rv[t], i < K, pt, qt, i < K);
+        __syncthreads();
+    }
 }
 
 // ----------------------------------------------------------- greedy --
@@ -946,7 +1084,7 @@ __global__ __launch_bounds__(kThreads) void sv_greedy_kernel(Args a)
     publish_part<M>(a, row, c, block_reduce<M, false>(thread_stats<M, kVecG>(x, x, c), 0));
     if (c != finisher_column(b, NC) || r != K) return;
 
-    const Outcome o = finish_rows<VEC, false, kVecG, M, M>(lds_greedy, a, b);
+    const Outcome o = finish_rows<VEC, false, kVecG, M, M>(lds_greedy, a, b, a.stats != nullptr);
     if (threadIdx.x == 0) {
         a.n_out[b] = o.n;
         a.next_out[b] = o.arg;
@@ -1230,12 +1368,14 @@ __device__ __forceinline__ void finish_bonus(const Args& a, int b)
             drawn = n < K;
         }
     }
-    if (STATS || n < 0) {
-        const Outcome o = finish_rows<VEC, true, kVecS, MP, MB>(lds.g, a, b);
+    if ((STATS && ROWS) || n < 0) {
+        const Outcome o = finish_rows<VEC, true, kVecS, MP, MB>(lds.g, a, b, STATS && ROWS);
         n = o.n;
         Pn = o.P;
         Qn = o.Q;
     }
+    // with statistics, the walks' finishing block writes every row's in tiles
+    if (STATS && !ROWS) write_all_stats<VEC, MP, MB>(a, b);
     if (!drawn) draw_and_write<VEC, MB>(a, b, n, Pn, Qn);
 }
 
