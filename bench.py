@@ -106,7 +106,7 @@ def _time_oracle(once, target_seconds):
 
 def cpu_baseline(cfg, mode, target_seconds=10.0, logits=False, tau=1.0):
     """Time the fp64 oracle as it stands over a bounded sample of the
-    workload (whole sequences of round 0), scaled to rounds/s: once on one
+    workload (whole sequences of input set 0), scaled to rounds/s: once on one
     thread and once on the host's cores (cpu_threads; the oracle splits a
     batch over threads by whole sequences).  The logits oracle is numpy on
     one thread, so it is timed once."""
@@ -134,7 +134,7 @@ def cpu_baseline(cfg, mode, target_seconds=10.0, logits=False, tau=1.0):
             else:
                 oracle.verify_greedy(args[0], args[2], threads=nthreads)
         reps, el = _time_oracle(once, target_seconds)
-        return reps * seqs / el / B, f"{seqs} of {B} sequences of round 0, repeated {reps}x in {el:.1f}s " \
+        return reps * seqs / el / B, f"{seqs} of {B} sequences of input set 0, repeated {reps}x in {el:.1f}s " \
                                      f"on {nthreads} thread(s), scaled by {seqs}/{B} to whole rounds"
 
     v1, s1 = run(1, min(n_seq, 2))
