@@ -1,14 +1,16 @@
 """Benchmark of the batched verification step on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
-                    [--mode sampled|greedy] [--no-cpu-baseline] [--no-ceiling]
+                    [--mode sampled|greedy] [--no-cpu-baseline] [--no-ceiling] [--no-settle]
 
 One step = one call of the verification library over a whole batch (all
 rows of all B sequences: the fused row pass, the acceptance decisions, the
 accept-prefix scan and the final draw).  Inputs are generated on the host by
 the seeded workload generator, copied to HBM before timing, and two input
 sets alternate so that consecutive steps never hit the same data in the
-256 MB Infinity Cache.
+256 MB Infinity Cache.  Before the W warm-up steps a plain streaming read
+of the same bytes runs for at least 50 ms (the GPU then runs the timed steps
+at its loaded clocks) and measures the empirical read ceiling.
 
 Printed: one JSON line (rank 0) with verify rounds/s as `value`, the
 roofline of the dominant kernel (formula bytes per launch over the average
@@ -146,6 +148,57 @@ def cpu_baseline(cfg, mode, target_seconds=10.0, logits=False, tau=1.0):
     return out
 
 
+def _probe_lib():
+    import ctypes
+    path = os.path.join(ROOT, "speculative_decoding_verification_row_amd", "libsv_probe.so")
+    if not os.path.exists(path):
+        return None
+    L = ctypes.CDLL(path)
+    P, SZ, I32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
+    L.sv_probe_blocks.argtypes = [SZ, SZ, I32, I32]
+    L.sv_probe_blocks.restype = ctypes.c_int64
+    L.sv_probe_read.argtypes = [P, SZ, P, SZ, I32, I32, P, P]
+    L.sv_probe_read.restype = I32
+    return L
+
+
+def _probe_buffers(sets, sampled):
+    bufs = []
+    for db in sets:
+        t, d = db["tp"], db["dp"] if sampled else None
+        bufs.append((t.data_ptr(), t.numel() * 4, d.data_ptr() if d is not None else None,
+                     d.numel() * 4 if d is not None else 0))
+    return bufs
+
+
+def settle_device(sets, sampled, min_ms=50.0):
+    """Stream the step's operand bytes with the read probe (one-shot shape)
+    for at least min_ms of wall clock before the warm-up steps, so that the
+    timed steps run at the GPU's loaded clocks.  Measured: straight after the
+    inputs are generated (the GPU idle while the host hashes them), 5 warm-up
+    steps of the headline workload leave the next 20 at 228.6-231.9 us per
+    launch, against 221.2 us over 400 after 40."""
+    import torch
+    L = _probe_lib()
+    if L is None:
+        return {"note": "libsv_probe.so not built; no settle"}
+    bufs = _probe_buffers(sets, sampled)
+    b0, b1 = bufs[0][1], bufs[0][3]
+    stream = torch.cuda.current_stream()
+    nb = L.sv_probe_blocks(b0, b1, 0, 0)
+    res = torch.empty(max(nb, 1), dtype=torch.float32, device=sets[0]["tp"].device)
+    t0, n = time.perf_counter(), 0
+    while True:
+        for _ in range(8):
+            x = bufs[n % len(bufs)]
+            assert L.sv_probe_read(x[0], x[1], x[2], x[3], 0, 0, res.data_ptr(), stream.cuda_stream) == 0
+            n += 1
+        torch.cuda.synchronize()
+        el = (time.perf_counter() - t0) * 1e3
+        if el >= min_ms:
+            return {"launches": n, "ms": round(el, 1)}
+
+
 def stream_ceiling(sets, sampled, steps=20):
     """The empirical ceiling of one read pass on this GPU: the streaming-read
     probe (libsv_probe.so; no arithmetic but a keep-alive sum) over the same
@@ -153,22 +206,11 @@ def stream_ceiling(sets, sampled, steps=20):
     chunk, and one persistent block per CU), two input sets alternating, one
     pair of HIP events around the timed launches.  Context for the roofline,
     never its peak."""
-    import ctypes
     import torch
-    path = os.path.join(ROOT, "speculative_decoding_verification_row_amd", "libsv_probe.so")
-    if not os.path.exists(path):
+    L = _probe_lib()
+    if L is None:
         return {"note": "libsv_probe.so not built"}
-    L = ctypes.CDLL(path)
-    P, SZ, I32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
-    L.sv_probe_blocks.argtypes = [SZ, SZ, I32, I32]
-    L.sv_probe_blocks.restype = ctypes.c_int64
-    L.sv_probe_read.argtypes = [P, SZ, P, SZ, I32, I32, P, P]
-    L.sv_probe_read.restype = I32
-    bufs = []
-    for db in sets:
-        t, d = db["tp"], db["dp"] if sampled else None
-        bufs.append((t.data_ptr(), t.numel() * 4, d.data_ptr() if d is not None else None,
-                     d.numel() * 4 if d is not None else 0))
+    bufs = _probe_buffers(sets, sampled)
     b0, b1 = bufs[0][1], bufs[0][3]
     stream = torch.cuda.current_stream()
     out = {"bytes_per_launch": b0 + b1, "unit": "GB/s", "steps": steps}
@@ -222,6 +264,9 @@ def main():
                     help="time rounds of the multi-round driver (B=1, K=4, V=32000) instead")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the streaming-read probe (the empirical ceiling reported beside the roofline)")
+    ap.add_argument("--no-settle", action="store_true",
+                    help="skip the >= 50 ms of streaming reads that bring the GPU to its loaded clocks "
+                         "before the warm-up steps")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy 5 times (reference for "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE scaling)")
@@ -291,6 +336,13 @@ def main():
             sv.sv_verify_greedy_batched(db["tp"], db["dt"], n_accepted=n_out, next_token=x_out,
                                         workspace=ws, stats=st_out, stream=stream)
 
+    # The read probe runs before the warm-up steps: first a settle of at
+    # least 50 ms, then (unless --no-ceiling) the ceiling measurement.
+    settle = settle_device(sets, sampled) if not args.no_settle else None
+    ceil = None
+    if not args.no_ceiling:
+        log("streaming-read probe over the same bytes (empirical ceiling, context)")
+        ceil = stream_ceiling(sets, sampled)
     for w in range(args.warmup):
         step(sets[w % len(sets)])
     torch.cuda.synchronize()
@@ -370,9 +422,9 @@ def main():
             torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
         line["copy_calibration_bytes"] = src.numel() * 4
-    if not args.no_ceiling:
-        log("streaming-read probe over the same bytes (empirical ceiling, context)")
-        ceil = stream_ceiling(sets, sampled)
+    if settle is not None:
+        line["settle"] = settle
+    if ceil is not None:
         if "gbs" in ceil:
             ceil["kernel_frac_of_ceiling"] = round(achieved / ceil["gbs"], 4)
         line["stream_ceiling"] = ceil
