@@ -1101,6 +1101,17 @@ struct Poll {
     float pt, qt, u;
 };
 
+// An empty asm that takes a value and gives it back.  Applied to polled
+// values once the step's row loads are issued, it keeps the compiler from
+// moving what is computed from them (the fp64 conversions of the acceptance
+// test) up to the polls themselves: waiting there, one poll after another,
+// would hold back the wave's row loads by as many round trips to memory.
+template <class T>
+__device__ __forceinline__ void settle(T& v)
+{
+    asm volatile("" : "+v"(v));
+}
+
 __device__ __forceinline__ Poll poll_issue(const Args& a, int b, int i, int tok)
 {
     Poll p{0ull, 0ull, 0.0f, 0.0f, 0.0f};
@@ -1524,7 +1535,14 @@ __global__ __launch_bounds__(kThreads, 4) void sv_sample_kernel(Args a)
         if (!EARLY) load_next(i);
         __builtin_amdgcn_sched_barrier(0);
         publish_part<MP>(a, row0 + i, c, block_reduce<MP, false>(thread_stats<MP, kVecS>(xp, xq, c), i & 1));
-        if (pending) decide(i - 1, pl);
+        if (pending) {
+            settle(pl.sp);
+            settle(pl.sq);
+            settle(pl.pt);
+            settle(pl.qt);
+            settle(pl.u);
+            decide(i - 1, pl);
+        }
         // the early exit issues row i+1's loads only once row i-1 is
         // accepted (or its decision is lost: the walk then still streams
         // every row), so that a rejection at n leaves rows n+2.. unread
@@ -2449,7 +2467,17 @@ __global__ __launch_bounds__(kThreads, 4) void sv_logits_kernel(Args a)
         if (!EARLY) load_next(i);
         __builtin_amdgcn_sched_barrier(0);
         publish_l(a, row0 + i, c, chunk_stats_l<kVecS, true>(xp, xq, c, V, kt, i & 1), true);
-        if (pending) decide(i - 1, pl);
+        if (pending) {
+            settle(pl.sp);
+            settle(pl.sq);
+            settle(pl.mp);
+            settle(pl.mq);
+            settle(pl.pt);
+            settle(pl.qt);
+            settle(pl.u);
+            settle(pl.tin);
+            decide(i - 1, pl);
+        }
         if (EARLY && state < 0) load_next(i);   // early exit: loads after the decision (searching or lost)
         if (state == kSearching) park(xp, xq);
 #pragma unroll
