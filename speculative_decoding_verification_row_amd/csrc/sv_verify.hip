@@ -192,6 +192,17 @@ __device__ __forceinline__ bool am_ok(unsigned long long w, unsigned ep) { retur
 __device__ __forceinline__ float am_val(unsigned long long w) { return __uint_as_float((unsigned)(w >> 32)); }
 __device__ __forceinline__ int am_arg(unsigned long long w) { return (int)((w >> 8) & 0xFFFFFFu); }
 
+// An empty asm that takes a value and gives it back.  Applied to polled
+// values once the step's row loads are issued, it keeps the compiler from
+// moving what is computed from them (the fp64 conversions of the acceptance
+// test) up to the polls themselves: waiting there, one poll after another,
+// would hold back the wave's row loads by as many round trips to memory.
+template <class T>
+__device__ __forceinline__ void settle(T& v)
+{
+    asm volatile("" : "+v"(v));
+}
+
 // Block-uniform bounded wait: true once the bound has passed (thread 0's
 // clock decides, so every thread leaves the wait loop together).
 __device__ __forceinline__ bool wait_expired(const Args& a, unsigned long long t0)
@@ -892,23 +903,38 @@ __device__ Outcome finish_rows(G& g, const Args& a, int b, bool write)
     bool done = false;
     for (int g0 = 0; g0 <= K; g0 += kGroup) {
         const int nrows = (K + 1 - g0) < kGroup ? (K + 1 - g0) : kGroup;
+        const int i = g0 + w;
+        // The token of row i loads while the partials are gathered, its
+        // values and the uniform while the row is combined; the values are
+        // settled (waited for) only after that, together.
+        int tk = -1;
+        if (w < nrows && lane == 0 && i < K) tk = a.dt[(int64_t)b * K + i];
         gather_rows<VEC, NV, MROW, MLAST>(g, a, b, g0, nrows);
         if (w < nrows) {
-            const int i = g0 + w;
             const int64_t row = (int64_t)b * (K + 1) + i;
             const bool pair = SAMPLED && i < K;
+            const bool tin = tk >= 0 && tk < V;
+            float pt = 0.0f, qt = 0.0f, u = 0.0f;
+            if (lane == 0 && (SAMPLED || write)) {
+                const int64_t x = tin ? tk : 0;
+                pt = a.tp[row * V + x];
+                if (pair) {
+                    qt = a.dp[((int64_t)b * K + i) * V + x];
+                    u = a.u[row];
+                }
+            }
             const RowView rv = i < K ? combine_row<MROW>(g, w, NC) : combine_row<MLAST>(g, w, NC);
             if (lane == 0) {
-                const int tk = i < K ? a.dt[(int64_t)b * K + i] : -1;
-                const bool tin = tk >= 0 && tk < V;
-                const float pt = tin ? a.tp[row * V + tk] : 0.0f;
-                float qt = 0.0f;
+                settle(pt);
+                settle(qt);
+                settle(u);
+                if (!tin) {
+                    pt = 0.0f;
+                    qt = 0.0f;
+                }
                 int rej = 0;
                 if (SAMPLED) {
-                    if (pair) {
-                        qt = tin ? a.dp[((int64_t)b * K + i) * V + tk] : 0.0f;
-                        rej = accepted(a.u[(int64_t)b * (K + 1) + i], pt, qt, rv.P, rv.Q) ? 0 : 1;
-                    }
+                    if (pair) rej = accepted(u, pt, qt, rv.P, rv.Q) ? 0 : 1;
                 } else {
                     rej = (i < K && tk != rv.arg) ? 1 : 0;
                 }
@@ -1101,15 +1127,16 @@ struct Poll {
     float pt, qt, u;
 };
 
-// An empty asm that takes a value and gives it back.  Applied to polled
-// values once the step's row loads are issued, it keeps the compiler from
-// moving what is computed from them (the fp64 conversions of the acceptance
-// test) up to the polls themselves: waiting there, one poll after another,
-// would hold back the wave's row loads by as many round trips to memory.
-template <class T>
-__device__ __forceinline__ void settle(T& v)
+
+// All polled values at once: their loads are then all issued before the
+// first wait, and waited for together.
+__device__ __forceinline__ void settle_poll(Poll& p)
 {
-    asm volatile("" : "+v"(v));
+    settle(p.sp);
+    settle(p.sq);
+    settle(p.pt);
+    settle(p.qt);
+    settle(p.u);
 }
 
 __device__ __forceinline__ Poll poll_issue(const Args& a, int b, int i, int tok)
@@ -1469,7 +1496,9 @@ __global__ __launch_bounds__(kThreads, 4) void sv_sample_kernel(Args a)
         publish_part<MP>(a, row, c, block_reduce<MP, false>(thread_stats<MP, kVecS>(xp, xq, c), 0));
         park(xp, xq);
         double P, Q;
-        const int rej = poll_decide(a, b, i, poll_issue(a, b, i, tok), &P, &Q);
+        Poll pl = poll_issue(a, b, i, tok);
+        settle_poll(pl);
+        const int rej = poll_decide(a, b, i, pl, &P, &Q);
         if (rej != 0) {   // rejected: the residual mass; undecided: marked for recomputing
             const double m = rej > 0 ? block_sum(parked_resid(P, Q)) : __builtin_nan("");
             if (threadIdx.x == 0) put_u64(&a.wpart[((int64_t)b * K + i) * NC + c], tag_f64(m, a.epoch));
@@ -1536,11 +1565,7 @@ __global__ __launch_bounds__(kThreads, 4) void sv_sample_kernel(Args a)
         __builtin_amdgcn_sched_barrier(0);
         publish_part<MP>(a, row0 + i, c, block_reduce<MP, false>(thread_stats<MP, kVecS>(xp, xq, c), i & 1));
         if (pending) {
-            settle(pl.sp);
-            settle(pl.sq);
-            settle(pl.pt);
-            settle(pl.qt);
-            settle(pl.u);
+            settle_poll(pl);
             decide(i - 1, pl);
         }
         // the early exit issues row i+1's loads only once row i-1 is
@@ -1574,7 +1599,9 @@ __global__ __launch_bounds__(kThreads, 4) void sv_sample_kernel(Args a)
         }
     }
     if (state == kSearching) {   // the last draft row's decision
-        decide(K - 1, poll_issue(a, b, K - 1, tok));
+        Poll pl = poll_issue(a, b, K - 1, tok);
+        settle_poll(pl);
+        decide(K - 1, pl);
         if (state == kSearching) state = K;   // every draft accepted
     }
     if (c != finisher_column(b, NC)) return;
@@ -1846,6 +1873,18 @@ struct PollL {
     float pt, qt, u;
     int tin;
 };
+
+__device__ __forceinline__ void settle_poll_l(PollL& p)
+{
+    settle(p.sp);
+    settle(p.sq);
+    settle(p.mp);
+    settle(p.mq);
+    settle(p.pt);
+    settle(p.qt);
+    settle(p.u);
+    settle(p.tin);
+}
 
 __device__ __forceinline__ PollL poll_issue_l(const Args& a, int b, int i, int tok)
 {
@@ -2415,7 +2454,9 @@ __global__ __launch_bounds__(kThreads, 4) void sv_logits_kernel(Args a)
         publish_l(a, row, c, chunk_stats_l<kVecS, true>(xp, xq, c, V, kt, 0), true);
         park(xp, xq);
         LRow r;
-        const int rej = poll_decide_l(a, b, i, poll_issue_l(a, b, i, tok), &r);
+        PollL pl = poll_issue_l(a, b, i, tok);
+        settle_poll_l(pl);
+        const int rej = poll_decide_l(a, b, i, pl, &r);
         if (rej != 0) {   // rejected: the residual mass; undecided: marked for recomputing
             const double m = rej > 0 ? block_sum(parked_resid_l(r, kt, c, V)) : __builtin_nan("");
             if (threadIdx.x == 0) put_u64(&a.wpart[((int64_t)b * K + i) * NC + c], tag_f64(m, a.epoch));
@@ -2468,14 +2509,7 @@ __global__ __launch_bounds__(kThreads, 4) void sv_logits_kernel(Args a)
         __builtin_amdgcn_sched_barrier(0);
         publish_l(a, row0 + i, c, chunk_stats_l<kVecS, true>(xp, xq, c, V, kt, i & 1), true);
         if (pending) {
-            settle(pl.sp);
-            settle(pl.sq);
-            settle(pl.mp);
-            settle(pl.mq);
-            settle(pl.pt);
-            settle(pl.qt);
-            settle(pl.u);
-            settle(pl.tin);
+            settle_poll_l(pl);
             decide(i - 1, pl);
         }
         if (EARLY && state < 0) load_next(i);   // early exit: loads after the decision (searching or lost)
@@ -2502,7 +2536,9 @@ __global__ __launch_bounds__(kThreads, 4) void sv_logits_kernel(Args a)
         }
     }
     if (state == kSearching) {
-        decide(K - 1, poll_issue_l(a, b, K - 1, tok));
+        PollL pl = poll_issue_l(a, b, K - 1, tok);
+        settle_poll_l(pl);
+        decide(K - 1, pl);
         if (state == kSearching) state = K;
     }
     if (c != finisher_column(b, NC)) return;
