@@ -1555,19 +1555,48 @@ __global__ __launch_bounds__(kThreads, 4) void sv_sample_kernel(Args a)
     };
 
     int i = 0;
+    if constexpr (STATS) {
+        // With statistics, step 0 (no decision pending yet) runs before the
+        // loop, so that where the loop reads (xp, xq) they always hold a
+        // copied row, never one still loading: the compiler then has no
+        // reason to wait there for the step's polls, issued just before the
+        // next row's loads, and the longer reduction of the statistics
+        // overlaps them (measured: 236.7 against 240.1 us at B=256 K=5
+        // V=128256; without statistics the same form measured 217.5 against
+        // 214.6 us, so that pass keeps the plain loop).
+        if (threadIdx.x == 0) tok = a.dt[(int64_t)b * K];   // row 0's token, for step 1
+        __builtin_amdgcn_sched_barrier(0);
+        if (!EARLY) load_next(0);
+        __builtin_amdgcn_sched_barrier(0);
+        publish_part<MP>(a, row0, c, block_reduce<MP, false>(thread_stats<MP, kVecS>(xp, xq, c), 0));
+        if (EARLY) load_next(0);
+        park(xp, xq);
+#pragma unroll
+        for (int k = 0; k < kVecS; ++k) {
+            xp[k] = yp[k];
+            xq[k] = yq[k];
+        }
+        // row 1 has arrived (the copy needs it anyway); the explicit wait
+        // tells the compiler so, which could otherwise hand row 1's load
+        // registers to the loop as still loading
+        __builtin_amdgcn_s_waitcnt(0);
+        i = 1;
+    }
     for (; i < K; ++i) {   // searching: decisions one step behind, rows parked
         Poll pl{0ull, 0ull, 0.0f, 0.0f, 0.0f};
-        const bool pending = i > 0;
+        const bool pending = STATS || i > 0;
         if (pending) pl = poll_issue(a, b, i - 1, tok);
         if (threadIdx.x == 0) tok = a.dt[(int64_t)b * K + i];   // row i's token, for step i+1
         __builtin_amdgcn_sched_barrier(0);
         if (!EARLY) load_next(i);
         __builtin_amdgcn_sched_barrier(0);
-        publish_part<MP>(a, row0 + i, c, block_reduce<MP, false>(thread_stats<MP, kVecS>(xp, xq, c), i & 1));
-        if (pending) {
-            settle_poll(pl);
-            decide(i - 1, pl);
-        }
+        // the polls are settled (waited for) after the reduction and before
+        // the partials are stored (a store issued after the row loads would
+        // make that wait cover some of them)
+        const Acc r = block_reduce<MP, false>(thread_stats<MP, kVecS>(xp, xq, c), i & 1);
+        if (pending) settle_poll(pl);
+        publish_part<MP>(a, row0 + i, c, r);
+        if (pending) decide(i - 1, pl);
         // the early exit issues row i+1's loads only once row i-1 is
         // accepted (or its decision is lost: the walk then still streams
         // every row), so that a rejection at n leaves rows n+2.. unread
