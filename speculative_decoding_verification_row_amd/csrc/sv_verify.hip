@@ -197,6 +197,8 @@ __device__ __forceinline__ int am_arg(unsigned long long w) { return (int)((w >>
 // moving what is computed from them (the fp64 conversions of the acceptance
 // test) up to the polls themselves: waiting there, one poll after another,
 // would hold back the wave's row loads by as many round trips to memory.
+// Applied to the thread index, it keeps what is computed from it where it
+// is written, instead of hoisted out of a loop and held (or spilled) there.
 template <class T>
 __device__ __forceinline__ void settle(T& v)
 {
@@ -1524,6 +1526,13 @@ __global__ __launch_bounds__(kThreads, 4) void sv_sample_kernel(Args a)
     double Pn = 0.0, Qn = 0.0;
     int tok = -1;                          // draft token of the pending row (thread 0)
     float4 xp[kVecS], xq[kVecS], yp[kVecS], yq[kVecS];
+    // While it searches, a walk's waves issue before those of walks that
+    // only stream (priority 2 of 0..3; the finishing block takes 3): the
+    // searching walks of a sequence move in step with their slowest sibling,
+    // so they, not the streaming ones, decide when the last walks end.
+    // Measured: 174.1 -> 171.8 us at B=32 K=16 V=262144, 1305.5 -> 1298.4 us
+    // at B=1024 K=8 V=128256, 214.9 -> 214.6 us at B=256 K=5 V=128256.
+    __builtin_amdgcn_s_setprio(2);
     load_chunk<VEC, kVecS>(row_of(tb, V), c, xp);
     load_chunk<VEC, kVecS>(row_of(db, V), c, xq);
 
@@ -1617,6 +1626,7 @@ __global__ __launch_bounds__(kThreads, 4) void sv_sample_kernel(Args a)
     // residual of row n); the row after n is already in flight.  A walk
     // that lost its decision still publishes every row, for the finisher.
     if (EARLY && state >= 0) i = K;
+    __builtin_amdgcn_s_setprio(0);   // searching is over: back to the default priority
     for (; i < K; ++i) {   // after the first rejection (or a lost decision)
         load_next(i);
         __builtin_amdgcn_sched_barrier(0);
@@ -1802,7 +1812,13 @@ __device__ __forceinline__ LStat chunk_stats_l(float4 (&pv)[NV], float4 (&qv)[NV
         mq = wave_maxf(share_max<NV>(qv));
         sq = wave_sum(share_wsum<NV>(qv, mq, k));
     }
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    // the wave's LDS address formed here at every call (as in poll_issue_l):
+    // kept for the whole walk it went to scratch, and its reload held every
+    // step's reduction until that step's row loads had arrived
+    // (234.8 -> 232.6 us at B=256 K=5 V=128256)
+    int tid = threadIdx.x;
+    settle(tid);
+    const int lane = tid & 63, w = tid >> 6;
     if (lane == 0) {
         s_m[slot][0][w] = mp;
         s_s[slot][0][w] = sp;
@@ -1918,7 +1934,13 @@ __device__ __forceinline__ void settle_poll_l(PollL& p)
 __device__ __forceinline__ PollL poll_issue_l(const Args& a, int b, int i, int tok)
 {
     PollL p{0ull, 0ull, 0ull, 0ull, 0.0f, 0.0f, 0.0f, 0};
-    const int t = threadIdx.x, K = a.K, V = a.V;
+    // The thread index passes through an empty asm so that the lane's word
+    // address is formed here at every call: hoisted out of the walk, it was
+    // one more value to keep for the whole walk, and at 128 VGPRs it went to
+    // scratch, whose reload waited (in order) for the row loads in flight.
+    int t = threadIdx.x;
+    settle(t);
+    const int K = a.K, V = a.V;
     const int64_t row = (int64_t)b * (K + 1) + i;
     if (t < a.NC && t < 64) {
         const Part* pp = a.parts + row * a.NC + t;
@@ -1949,7 +1971,9 @@ __device__ int poll_decide_l(const Args& a, int b, int i, PollL pl, LRow* out)
 {
     __shared__ LRow s_row;
     __shared__ int s_rej;
-    const int NC = a.NC, t = threadIdx.x;
+    const int NC = a.NC;
+    int t = threadIdx.x;
+    settle(t);   // as in poll_issue_l: addresses formed here, not kept in scratch
     const unsigned ep = a.epoch;
     const float k = a.ktau;
     const int64_t row = (int64_t)b * (a.K + 1) + i;
@@ -2502,6 +2526,7 @@ __global__ __launch_bounds__(kThreads, 4) void sv_logits_kernel(Args a)
     LRow rn{0.0, 0.0, 0.0f, 0.0f};
     int tok = -1;
     float4 xp[kVecS], xq[kVecS], yp[kVecS], yq[kVecS];
+    __builtin_amdgcn_s_setprio(2);   // searching walks first, as in the probabilities walk (236.3 -> 235.0 us)
     load_chunk<VEC, kVecS>(row_of(tb, V), c, xp);
     load_chunk<VEC, kVecS>(row_of(db, V), c, xq);
 
@@ -2554,6 +2579,7 @@ __global__ __launch_bounds__(kThreads, 4) void sv_logits_kernel(Args a)
         }
     }
     if (EARLY && state >= 0) i = K;   // early exit: no row after a decided rejection
+    __builtin_amdgcn_s_setprio(0);
     for (; i < K; ++i) {
         load_next(i);
         __builtin_amdgcn_sched_barrier(0);
