@@ -1793,10 +1793,10 @@ struct LStat {
 
 // Block-cooperative: (m_c, s_c) of target chunk pv and, with Q, of draft
 // chunk qv, valid in thread 0.  Each wave sums its weights against its own
-// maximum (found by DPP, no barrier); thread 0 takes the chunk maximum m_c
-// over the four waves and rescales their sums to it, in wave order.  The
-// positions of pv and qv at or past V are set to -inf (mask_tail_l).
-// Consecutive calls alternate `slot`, as for block_reduce.
+// maximum (found by DPP, no barrier); wave 0 takes the chunk maximum m_c
+// over the four waves and rescales their sums to it, adding them in wave
+// order.  The positions of pv and qv at or past V are set to -inf
+// (mask_tail_l).  Consecutive calls alternate `slot`, as for block_reduce.
 template <int NV, bool Q>
 __device__ __forceinline__ LStat chunk_stats_l(float4 (&pv)[NV], float4 (&qv)[NV], int c, int V, float k, int slot)
 {
@@ -1827,18 +1827,27 @@ __device__ __forceinline__ LStat chunk_stats_l(float4 (&pv)[NV], float4 (&qv)[NV
     }
     __syncthreads();
     LStat r{mp, mq, 0.0, 0.0};
-    if (threadIdx.x == 0) {
-        for (int o = 0; o < (Q ? 2 : 1); ++o) {
-            float M = s_m[slot][o][0];
-            for (int j = 1; j < kWaves; ++j) M = fmaxf(M, s_m[slot][o][j]);
-            double S = 0.0;
-            for (int j = 0; j < kWaves; ++j) S += chunk_scaled(s_m[slot][o][j], s_s[slot][o][j], M, k);
-            if (o == 0) {
-                r.mp = M;
-                r.sp = S;
-            } else {
-                r.mq = M;
-                r.sq = S;
+    if (tid < 64) {
+        // Lane 4 o + j of wave 0 rescales wave j's sum of operand o (one
+        // exp2 each, side by side rather than eight in a row on one lane);
+        // the four terms of an operand are then added in wave order, the
+        // sum one lane would form (230.9 against 232.0 us at B=256 K=5
+        // V=128256).  Lanes 8..63 repeat lanes 0..7.
+        static_assert(kWaves == 4, "one lane per (operand, wave) pair in a group of four");
+        const int o = Q ? (lane >> 2) & 1 : 0, j = lane & 3, g = lane & ~3;
+        float M = s_m[slot][o][0];
+        for (int jj = 1; jj < kWaves; ++jj) M = fmaxf(M, s_m[slot][o][jj]);
+        const double t = chunk_scaled(s_m[slot][o][j], s_s[slot][o][j], M, k);
+        const double t1 = __shfl(t, g + 1), t2 = __shfl(t, g + 2), t3 = __shfl(t, g + 3);
+        const double S = ((t + t1) + t2) + t3;
+        const double Sq = __shfl(S, 4);
+        const float Mq = __shfl(M, 4);
+        if (lane == 0) {
+            r.mp = M;
+            r.sp = S;
+            if (Q) {
+                r.mq = Mq;
+                r.sq = Sq;
             }
         }
     }
@@ -2545,50 +2554,70 @@ __global__ __launch_bounds__(kThreads, 4) void sv_logits_kernel(Args a)
             if (threadIdx.x == 0) put_u64(&a.wpart[((int64_t)b * K + j) * NC + c], tag_f64(w, a.epoch));
         }
     };
-    auto load_next = [&](int i) {
+    // Row i+1's loads into (p, q) (an empty range after the last draft row
+    // reads zeros).  The logits walk keeps its two row buffers by turns: the
+    // row of one step is computed where the previous step loaded it, so the
+    // next row's loads leave without first waiting for that row and copying
+    // it over (the arithmetic of a logits row is long enough for this to
+    // show: 232.2 -> 229.6 us at B=256 K=5 V=128256; the probabilities walk
+    // measured no difference).  Functions taking the buffers are inlined:
+    // out of line they would take the kernel arguments' address.
+    auto load_to = [&](int i, float4 (&p)[kVecS], float4 (&q)[kVecS]) __attribute__((always_inline)) {
         const bool more = i + 1 < K;
         const int64_t off = more ? (int64_t)(i + 1) * V : 0;
-        load_chunk<VEC, kVecS>(row_of(tb + off, more ? V : 0), c, yp);
-        load_chunk<VEC, kVecS>(row_of(db + off, more ? V : 0), c, yq);
+        load_chunk<VEC, kVecS>(row_of(tb + off, more ? V : 0), c, p);
+        load_chunk<VEC, kVecS>(row_of(db + off, more ? V : 0), c, q);
     };
-
-    int i = 0;
-    for (; i < K; ++i) {
+    // one searching step: row i in (cp, cq), row i+1 loading into (np, nq)
+    auto search_step = [&](int i, float4 (&cp)[kVecS], float4 (&cq)[kVecS], float4 (&np)[kVecS],
+                           float4 (&nq)[kVecS]) __attribute__((always_inline)) {
         PollL pl{0ull, 0ull, 0ull, 0ull, 0.0f, 0.0f, 0.0f, 0};
         const bool pending = i > 0;
         if (pending) pl = poll_issue_l(a, b, i - 1, tok);
         if (threadIdx.x == 0) tok = a.dt[(int64_t)b * K + i];
         __builtin_amdgcn_sched_barrier(0);
-        if (!EARLY) load_next(i);
+        if (!EARLY) load_to(i, np, nq);
         __builtin_amdgcn_sched_barrier(0);
-        publish_l(a, row0 + i, c, chunk_stats_l<kVecS, true>(xp, xq, c, V, kt, i & 1), true);
+        publish_l(a, row0 + i, c, chunk_stats_l<kVecS, true>(cp, cq, c, V, kt, i & 1), true);
         if (pending) {
             settle_poll_l(pl);
             decide(i - 1, pl);
         }
-        if (EARLY && state < 0) load_next(i);   // early exit: loads after the decision (searching or lost)
-        if (state == kSearching) park(xp, xq);
+        if (EARLY && state < 0) load_to(i, np, nq);   // early exit: loads after the decision (searching or lost)
+        if (state == kSearching) park(cp, cq);
+    };
+
+    int i = 0;
+    while (i < K) {   // two steps a turn; the row of the step after the loop is left in (xp, xq)
+        search_step(i, xp, xq, yp, yq);
+        ++i;
+        if (state != kSearching || i >= K) {
 #pragma unroll
-        for (int j = 0; j < kVecS; ++j) {
-            xp[j] = yp[j];
-            xq[j] = yq[j];
-        }
-        if (state != kSearching) {
-            ++i;
+            for (int j = 0; j < kVecS; ++j) {
+                xp[j] = yp[j];
+                xq[j] = yq[j];
+            }
             break;
         }
+        search_step(i, yp, yq, xp, xq);
+        ++i;
+        if (state != kSearching) break;
     }
     if (EARLY && state >= 0) i = K;   // early exit: no row after a decided rejection
     __builtin_amdgcn_s_setprio(0);
-    for (; i < K; ++i) {
-        load_next(i);
+    for (; i + 1 < K; i += 2) {   // streaming, also two rows a turn
+        load_to(i, yp, yq);
         __builtin_amdgcn_sched_barrier(0);
         publish_l(a, row0 + i, c, chunk_stats_l<kVecS, true>(xp, xq, c, V, kt, i & 1), true);
-#pragma unroll
-        for (int j = 0; j < kVecS; ++j) {
-            xp[j] = yp[j];
-            xq[j] = yq[j];
-        }
+        load_to(i + 1, xp, xq);
+        __builtin_amdgcn_sched_barrier(0);
+        publish_l(a, row0 + i + 1, c, chunk_stats_l<kVecS, true>(yp, yq, c, V, kt, (i + 1) & 1), true);
+    }
+    if (i < K) {
+        load_to(i, yp, yq);
+        __builtin_amdgcn_sched_barrier(0);
+        publish_l(a, row0 + i, c, chunk_stats_l<kVecS, true>(xp, xq, c, V, kt, i & 1), true);
+        ++i;
     }
     if (state == kSearching) {
         PollL pl = poll_issue_l(a, b, K - 1, tok);
