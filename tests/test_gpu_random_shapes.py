@@ -19,7 +19,7 @@ from _forms import set_form
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
-N_SHAPES = 24
+N_SHAPES = 64
 
 
 def _case(msg):
