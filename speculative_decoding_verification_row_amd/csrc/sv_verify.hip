@@ -415,9 +415,11 @@ __device__ __forceinline__ double thread_resid_reload(Row prow, Row qrow, int c,
 // and the two partners compute the same commutative sum or merge).
 constexpr int kDppPairs = 0xB1, kDppQuads = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
 
-// Each of the four controls is a permutation of the row (every lane has a
-// source), so the move needs no prior value in its destination: a plain DPP
-// move, not an update of a zeroed register (one VALU move fewer per step).
+// Every control used with it gives every lane a source lane (the four above
+// permute a row; quad broadcasts such as 0x55, lane 1 of each quad to the
+// whole quad, are used too), so the move needs no prior value in its
+// destination: a plain DPP move, not an update of a zeroed register (one
+// VALU move fewer per step).
 template <int CTRL>
 __device__ __forceinline__ int dpp_i32(int v)
 {
@@ -491,21 +493,27 @@ __device__ __forceinline__ void argmax_step(float& v, int& i)
 }
 
 // (value, index) maximum over the wave (all 64 lanes active), the same in
-// every lane.
+// every lane.  The rows' results merge as (r0 . r1) . (r2 . r3) by the lane
+// swaps; the merge (larger value, then lower index) is associative on finite
+// values, so this is the pair the row-order scan of lanes 0, 16, 32, 48 gave
+// (greedy 115.5 -> 115.0 us at B=256 K=5 V=128256).
 __device__ __forceinline__ void wave_argmax(float& v, int& i)
 {
     argmax_step<kDppPairs>(v, i);
     argmax_step<kDppQuads>(v, i);
     argmax_step<kDppHalfMirror>(v, i);
     argmax_step<kDppMirror>(v, i);
-    float bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-    int bi = __builtin_amdgcn_readlane(i, 0);
-#pragma unroll
-    for (int r = 1; r < 4; ++r)
-        argmax_merge(bv, bi, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16 * r)),
-                     __builtin_amdgcn_readlane(i, 16 * r));
-    v = bv;
-    i = bi;
+    unsigned av, bv, ai, bi;
+    rows_01_23(__float_as_uint(v), av, bv);
+    rows_01_23((unsigned)i, ai, bi);
+    float mv = __uint_as_float(av);
+    int mi = (int)ai;
+    argmax_merge(mv, mi, __uint_as_float(bv), (int)bi);
+    halves(__float_as_uint(mv), av, bv);
+    halves((unsigned)mi, ai, bi);
+    v = __uint_as_float(av);
+    i = (int)ai;
+    argmax_merge(v, i, __uint_as_float(bv), (int)bi);
 }
 
 __device__ __forceinline__ double wave_inclusive_scan(double v)
@@ -1875,10 +1883,14 @@ __device__ __forceinline__ LStat chunk_stats_l(float4 (&pv)[NV], float4 (&qv)[NV
         float M = s_m[slot][o][0];
         for (int jj = 1; jj < kWaves; ++jj) M = fmaxf(M, s_m[slot][o][jj]);
         const double t = chunk_scaled(s_m[slot][o][j], s_s[slot][o][j], M, k);
-        const double t1 = __shfl(t, g + 1), t2 = __shfl(t, g + 2), t3 = __shfl(t, g + 3);
+        // lanes g+1..g+3 of the quad by DPP, lane 4's results by scalar reads
+        const double t1 = dpp_f64<0x55>(t), t2 = dpp_f64<0xAA>(t), t3 = dpp_f64<0xFF>(t);
         const double S = ((t + t1) + t2) + t3;
-        const double Sq = __shfl(S, 4);
-        const float Mq = __shfl(M, 4);
+        const unsigned long long sb = (unsigned long long)__double_as_longlong(S);
+        const double Sq = __longlong_as_double(
+            (long long)(((unsigned long long)(unsigned)__builtin_amdgcn_readlane((int)(sb >> 32), 4) << 32) |
+                        (unsigned)__builtin_amdgcn_readlane((int)sb, 4)));
+        const float Mq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(M), 4));
         if (lane == 0) {
             r.mp = M;
             r.sp = S;
